@@ -1,0 +1,330 @@
+// Host side of the C ABI declared in include/wf_chunk_attn.h: argument
+// validation, cache metadata, chunk scheduling and kernel launch.
+//
+// Every check runs before anything is enqueued, so a non-OK status leaves the
+// device and the cache metadata untouched.
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "wf_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+wf_status fail(wf_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+wf_status ok() {
+  g_err.clear();
+  return WF_OK;
+}
+
+int esize_of(int32_t dt) {
+  switch (dt) {
+    case WF_F32: return 4;
+    case WF_BF16: return 2;
+    case WF_FP8_E4M3: return 1;
+    default: return 0;
+  }
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool overlap(const void* a, uint64_t na, const void* b, uint64_t nb) {
+  if (na == 0 || nb == 0) return false;
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+// Structural checks of a cache description (not the live window).
+wf_status check_layout(const wf_kv_cache* c) {
+  if (c == nullptr) return fail(WF_ERR_INVALID_ARG, "cache is NULL");
+  const int es = esize_of(c->kv_dtype);
+  if (es == 0) return fail(WF_ERR_UNSUPPORTED, "kv_dtype %d is not F32, BF16 or FP8_E4M3", c->kv_dtype);
+  if (c->head_dim != 64 && c->head_dim != 128)
+    return fail(WF_ERR_UNSUPPORTED, "head_dim %d not built (64 or 128)", c->head_dim);
+  if (c->num_heads < 1 || c->num_heads > 4096)
+    return fail(WF_ERR_INVALID_ARG, "num_heads %d out of range [1, 4096]", c->num_heads);
+  if (c->page_size < 8 || c->page_size % 8 != 0)
+    return fail(WF_ERR_UNSUPPORTED, "page_size %d must be a positive multiple of 8", c->page_size);
+  if (c->table_len < 1 || c->table_len > WF_MAX_TABLE_LEN)
+    return fail(WF_ERR_INVALID_ARG, "table_len %d out of range [1, %d]", c->table_len, WF_MAX_TABLE_LEN);
+  if (c->num_pages < c->table_len)
+    return fail(WF_ERR_INVALID_ARG, "num_pages %d < table_len %d", c->num_pages, c->table_len);
+  if ((int64_t)c->table_len * c->page_size >= (int64_t)1 << 30)
+    return fail(WF_ERR_UNSUPPORTED, "capacity table_len*page_size must stay below 2^30 tokens");
+  if (c->page_table == nullptr) return fail(WF_ERR_INVALID_ARG, "page_table is NULL");
+  std::vector<char> seen(c->num_pages, 0);
+  for (int i = 0; i < c->table_len; ++i) {
+    const int32_t pg = c->page_table[i];
+    if (pg < 0 || pg >= c->num_pages)
+      return fail(WF_ERR_INVALID_ARG, "page_table[%d] = %d outside [0, %d)", i, pg, c->num_pages);
+    if (seen[pg]) return fail(WF_ERR_INVALID_ARG, "page_table names page %d twice", pg);
+    seen[pg] = 1;
+  }
+  if (c->k == nullptr || c->v == nullptr) return fail(WF_ERR_INVALID_ARG, "cache k/v pointer is NULL");
+  if (!aligned(c->k, 16) || !aligned(c->v, 16))
+    return fail(WF_ERR_INVALID_ARG, "cache k/v pointers must be 16-byte aligned");
+  if (c->kv_dtype == WF_FP8_E4M3) {
+    if (c->k_scale == nullptr || c->v_scale == nullptr)
+      return fail(WF_ERR_INVALID_ARG, "E4M3FN cache needs k_scale and v_scale");
+    if (!aligned(c->k_scale, 4) || !aligned(c->v_scale, 4))
+      return fail(WF_ERR_INVALID_ARG, "scale pointers must be 4-byte aligned");
+  }
+  const uint64_t kvb = (uint64_t)c->num_pages * c->num_heads * c->page_size * c->head_dim * es;
+  if (overlap(c->k, kvb, c->v, kvb)) return fail(WF_ERR_INVALID_ARG, "cache k and v buffers overlap");
+  return WF_OK;
+}
+
+wf_status check_window(const wf_kv_cache* c) {
+  const int64_t cap = (int64_t)c->table_len * c->page_size;
+  if (c->start < 0 || c->end < c->start || c->end > c->start + cap)
+    return fail(WF_ERR_INVALID_ARG, "window [%lld, %lld) invalid for capacity %lld", (long long)c->start,
+                (long long)c->end, (long long)cap);
+  return WF_OK;
+}
+
+uint64_t kv_bytes_of(const wf_kv_cache* c) {
+  return (uint64_t)c->num_pages * c->num_heads * c->page_size * c->head_dim * esize_of(c->kv_dtype);
+}
+
+wf::PageMap page_map(const wf_kv_cache* c, int64_t base) {
+  wf::PageMap m;
+  m.base_slot = (int32_t)((base / c->page_size) % c->table_len);
+  m.base_off = (int32_t)(base % c->page_size);
+  return m;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* wf_last_error(void) { return g_err.c_str(); }
+
+const char* wf_version(void) { return "wf_chunk_attn 0.1 gfx950"; }
+
+wf_status wf_kv_cache_check(const wf_kv_cache* c) {
+  wf_status s = check_layout(c);
+  if (s != WF_OK) return s;
+  s = check_window(c);
+  if (s != WF_OK) return s;
+  return ok();
+}
+
+wf_status wf_kv_cache_bytes(const wf_kv_cache* c, uint64_t* kv_bytes, uint64_t* scale_bytes) {
+  if (c == nullptr || kv_bytes == nullptr || scale_bytes == nullptr)
+    return fail(WF_ERR_INVALID_ARG, "NULL argument");
+  const int es = esize_of(c->kv_dtype);
+  if (es == 0) return fail(WF_ERR_UNSUPPORTED, "kv_dtype %d unknown", c->kv_dtype);
+  if (c->num_pages < 1 || c->num_heads < 1 || c->page_size < 1 || c->head_dim < 1)
+    return fail(WF_ERR_INVALID_ARG, "sizes must be positive");
+  *kv_bytes = kv_bytes_of(c);
+  const uint64_t nblk = (c->page_size + WF_SCALE_BLOCK - 1) / WF_SCALE_BLOCK;
+  *scale_bytes = c->kv_dtype == WF_FP8_E4M3 ? (uint64_t)c->num_pages * c->num_heads * nblk * 4 : 0;
+  return ok();
+}
+
+wf_status wf_kv_append(wf_kv_cache* c, int64_t pos, int32_t n, const void* k_new, const void* v_new,
+                       const float* k_scale_new, const float* v_scale_new, void* stream) {
+  wf_status s = check_layout(c);
+  if (s != WF_OK) return s;
+  if ((s = check_window(c)) != WF_OK) return s;
+  if (n < 0) return fail(WF_ERR_INVALID_ARG, "n = %d is negative", n);
+  if (pos < c->start || pos > c->end)
+    return fail(WF_ERR_RANGE, "append position %lld outside [start %lld, end %lld]", (long long)pos,
+                (long long)c->start, (long long)c->end);
+  const int64_t cap = (int64_t)c->table_len * c->page_size;
+  if (pos + n > c->start + cap)
+    return fail(WF_ERR_CAPACITY, "append [%lld, %lld) overruns live tokens (start %lld, capacity %lld)",
+                (long long)pos, (long long)(pos + n), (long long)c->start, (long long)cap);
+  if (n == 0) return ok();
+  if (k_new == nullptr || v_new == nullptr) return fail(WF_ERR_INVALID_ARG, "k_new/v_new is NULL");
+  if (!aligned(k_new, 16) || !aligned(v_new, 16))
+    return fail(WF_ERR_INVALID_ARG, "k_new/v_new must be 16-byte aligned");
+  const int es = esize_of(c->kv_dtype);
+  const uint64_t nb = (uint64_t)n * c->num_heads * c->head_dim * es;
+  const uint64_t kvb = kv_bytes_of(c);
+  if (overlap(k_new, nb, c->k, kvb) || overlap(k_new, nb, c->v, kvb) || overlap(v_new, nb, c->k, kvb) ||
+      overlap(v_new, nb, c->v, kvb))
+    return fail(WF_ERR_INVALID_ARG, "new K/V overlap the cache buffers");
+  const int nblk = (c->page_size + WF_SCALE_BLOCK - 1) / WF_SCALE_BLOCK;
+  if (c->kv_dtype == WF_FP8_E4M3) {
+    if (pos % c->page_size != 0 || n % c->page_size != 0)
+      return fail(WF_ERR_INVALID_ARG, "E4M3FN appends must be whole pages (pos %lld, n %d, page %d)",
+                  (long long)pos, n, c->page_size);
+    if (k_scale_new == nullptr || v_scale_new == nullptr)
+      return fail(WF_ERR_INVALID_ARG, "E4M3FN append needs k_scale_new and v_scale_new");
+    if (!aligned(k_scale_new, 4) || !aligned(v_scale_new, 4))
+      return fail(WF_ERR_INVALID_ARG, "scale pointers must be 4-byte aligned");
+  }
+  wf::AppendParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.k_new = k_new;
+  p.v_new = v_new;
+  p.ks_new = c->kv_dtype == WF_FP8_E4M3 ? k_scale_new : nullptr;
+  p.vs_new = c->kv_dtype == WF_FP8_E4M3 ? v_scale_new : nullptr;
+  p.k = c->k;
+  p.v = c->v;
+  p.ks = c->k_scale;
+  p.vs = c->v_scale;
+  p.n = n;
+  p.H = c->num_heads;
+  p.D = c->head_dim;
+  p.P = c->page_size;
+  p.T = c->table_len;
+  p.nblk = nblk;
+  p.esize = es;
+  p.lead = (int32_t)(pos % 64);
+  p.map = page_map(c, pos - p.lead);
+  p.divP = wf::make_fastdiv((uint32_t)c->page_size);
+  p.divT = wf::make_fastdiv((uint32_t)c->table_len);
+  std::memcpy(p.table, c->page_table, sizeof(int32_t) * c->table_len);
+  const int ntiles = (p.lead + n + 63) / 64;
+  hipError_t e = wf::launch_append(p, ntiles, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(WF_ERR_HIP, "append launch failed: %s", hipGetErrorString(e));
+  c->end = std::max(c->end, pos + n);
+  return ok();
+}
+
+wf_status wf_kv_evict(wf_kv_cache* c, int32_t n, uint32_t flags, void* stream) {
+  wf_status s = check_layout(c);
+  if (s != WF_OK) return s;
+  if ((s = check_window(c)) != WF_OK) return s;
+  if (n < 0 || (int64_t)n > c->end - c->start)
+    return fail(WF_ERR_RANGE, "cannot evict %d tokens from a window of %lld", n, (long long)(c->end - c->start));
+  if (flags & ~WF_EVICT_POISON) return fail(WF_ERR_INVALID_ARG, "unknown evict flags 0x%x", flags);
+  if ((flags & WF_EVICT_POISON) && n > 0) {
+    wf::PoisonParams p;
+    std::memset(&p, 0, sizeof(p));
+    p.k = c->k;
+    p.v = c->v;
+    p.n = n;
+    p.H = c->num_heads;
+    p.D = c->head_dim;
+    p.P = c->page_size;
+    p.T = c->table_len;
+    p.esize = esize_of(c->kv_dtype);
+    p.map = page_map(c, c->start);
+    p.divP = wf::make_fastdiv((uint32_t)c->page_size);
+    p.divT = wf::make_fastdiv((uint32_t)c->table_len);
+    std::memcpy(p.table, c->page_table, sizeof(int32_t) * c->table_len);
+    hipError_t e = wf::launch_poison(p, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(WF_ERR_HIP, "poison launch failed: %s", hipGetErrorString(e));
+  }
+  c->start += n;
+  return ok();
+}
+
+wf_status wf_chunk_attn_fwd(const wf_kv_cache* c, const void* q, int32_t q_dtype, void* o, float* lse,
+                            int32_t num_chunks, const int32_t* q_off, const int64_t* kv_begin,
+                            const int64_t* kv_end, float softmax_scale, void* stream) {
+  wf_status s = check_layout(c);
+  if (s != WF_OK) return s;
+  if ((s = check_window(c)) != WF_OK) return s;
+  const int kvd = c->kv_dtype;
+  const bool pair_ok = (q_dtype == WF_F32 && kvd == WF_F32) || (q_dtype == WF_BF16 && kvd == WF_BF16) ||
+                       (q_dtype == WF_BF16 && kvd == WF_FP8_E4M3);
+  if (!pair_ok)
+    return fail(WF_ERR_UNSUPPORTED, "(q_dtype %d, kv_dtype %d) not built: use (F32,F32), (BF16,BF16) or "
+                "(BF16,FP8_E4M3)", q_dtype, kvd);
+  if (num_chunks < 1 || num_chunks > WF_MAX_CHUNKS)
+    return fail(WF_ERR_INVALID_ARG, "num_chunks %d out of range [1, %d]", num_chunks, WF_MAX_CHUNKS);
+  if (q_off == nullptr || kv_begin == nullptr || kv_end == nullptr)
+    return fail(WF_ERR_INVALID_ARG, "chunk tables must not be NULL");
+  if (q_off[0] != 0) return fail(WF_ERR_INVALID_ARG, "q_off[0] must be 0");
+  for (int i = 0; i < num_chunks; ++i) {
+    if (q_off[i + 1] < q_off[i]) return fail(WF_ERR_INVALID_ARG, "q_off must be non-decreasing (chunk %d)", i);
+    if (!(c->start <= kv_begin[i] && kv_begin[i] < kv_end[i] && kv_end[i] <= c->end))
+      return fail(WF_ERR_RANGE, "chunk %d key range [%lld, %lld) empty or outside the live window [%lld, %lld)",
+                  i, (long long)kv_begin[i], (long long)kv_end[i], (long long)c->start, (long long)c->end);
+  }
+  const int64_t nq = q_off[num_chunks];
+  if (nq * c->num_heads >= ((int64_t)1 << 31))
+    return fail(WF_ERR_UNSUPPORTED, "too many query rows (%lld x %d heads)", (long long)nq, c->num_heads);
+  if (!(std::isfinite(softmax_scale))) return fail(WF_ERR_INVALID_ARG, "softmax_scale is not finite");
+  if (nq == 0) return ok();
+  if (q == nullptr || o == nullptr) return fail(WF_ERR_INVALID_ARG, "q/o is NULL");
+  if (!aligned(q, 16) || !aligned(o, 16)) return fail(WF_ERR_INVALID_ARG, "q/o must be 16-byte aligned");
+  if (lse != nullptr && !aligned(lse, 4)) return fail(WF_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  const uint64_t qb = (uint64_t)nq * c->num_heads * c->head_dim * esize_of(q_dtype);
+  const uint64_t kvb = kv_bytes_of(c);
+  if (overlap(o, qb, q, qb) || overlap(o, qb, c->k, kvb) || overlap(o, qb, c->v, kvb))
+    return fail(WF_ERR_INVALID_ARG, "o overlaps q or the cache");
+  if (lse != nullptr) {
+    const uint64_t lb = (uint64_t)nq * c->num_heads * 4;
+    if (overlap(lse, lb, o, qb) || overlap(lse, lb, q, qb) || overlap(lse, lb, c->k, kvb) ||
+        overlap(lse, lb, c->v, kvb))
+      return fail(WF_ERR_INVALID_ARG, "lse overlaps q, o or the cache");
+  }
+
+  wf::AttnParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.q = q;
+  p.o = o;
+  p.lse = lse;
+  p.k = c->k;
+  p.v = c->v;
+  p.ks = c->k_scale;
+  p.vs = c->v_scale;
+  p.nq = (int32_t)nq;
+  p.H = c->num_heads;
+  p.P = c->page_size;
+  p.T = c->table_len;
+  p.nblk = (c->page_size + WF_SCALE_BLOCK - 1) / WF_SCALE_BLOCK;
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)c->head_dim);
+  p.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  p.divP = wf::make_fastdiv((uint32_t)c->page_size);
+  p.divT = wf::make_fastdiv((uint32_t)c->table_len);
+  std::memcpy(p.table, c->page_table, sizeof(int32_t) * c->table_len);
+
+  // Longest-processing-time-first order: chunks with the most (query x key) work are issued first.
+  std::vector<int> order;
+  for (int i = 0; i < num_chunks; ++i)
+    if (q_off[i + 1] > q_off[i]) order.push_back(i);
+  std::stable_sort(order.begin(), order.end(), [&](int a, int b) {
+    const int64_t wa = (int64_t)(q_off[a + 1] - q_off[a]) * (kv_end[a] - kv_begin[a]);
+    const int64_t wb = (int64_t)(q_off[b + 1] - q_off[b]) * (kv_end[b] - kv_begin[b]);
+    return wa > wb;
+  });
+  int64_t items = 0;
+  int nc = 0;
+  for (int i : order) {
+    wf::ChunkDesc& d = p.chunk[nc++];
+    d.q_begin = q_off[i];
+    d.q_len = q_off[i + 1] - q_off[i];
+    d.ntiles = (d.q_len + wf::kBlockM - 1) / wf::kBlockM;
+    d.item0 = (int32_t)items;
+    d.lead = (int32_t)(kv_begin[i] % 8);
+    d.nkeys = (int32_t)(kv_end[i] - kv_begin[i]);
+    d.map = page_map(c, kv_begin[i] - d.lead);
+    items += (int64_t)d.ntiles * c->num_heads;
+  }
+  p.num_chunks = nc;
+  p.num_items = (int32_t)items;
+  if (items == 0) return ok();
+
+  hipError_t e;
+  if (q_dtype == WF_F32)
+    e = wf::launch_attn_f32(p, c->head_dim, (hipStream_t)stream);
+  else if (kvd == WF_BF16)
+    e = wf::launch_attn_bf16(p, c->head_dim, (hipStream_t)stream);
+  else
+    e = wf::launch_attn_fp8kv(p, c->head_dim, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(WF_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,117 @@
+// Internal kernel parameter blocks and launchers shared by the host layer
+// (api.cpp) and the HIP kernels.  Not part of the public ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/wf_chunk_attn.h"
+
+namespace wf {
+
+// Unsigned 32-bit division by a runtime-invariant divisor via multiply-high
+// (round-up method, Granlund & Montgomery 1994 / Hacker's Delight 10-8).
+// Exact for every n < 2^32 and 1 <= d < 2^31.
+struct FastDiv {
+  uint32_t d;      // divisor
+  uint32_t mult;   // magic multiplier
+  uint32_t shift;  // ceil(log2 d)
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+  FastDiv f;
+  f.d = d;
+  uint32_t l = 0;
+  while ((1ull << l) < d) ++l;
+  f.shift = l;
+  f.mult = (uint32_t)((((1ull << l) - d) << 32) / d + 1);
+  return f;
+}
+
+__host__ __device__ inline uint32_t fastdiv(uint32_t n, const FastDiv& f) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  uint32_t t = __umulhi(n, f.mult);
+#else
+  uint32_t t = (uint32_t)(((uint64_t)n * f.mult) >> 32);
+#endif
+  if (f.shift == 0) return n;  // d == 1
+  return (t + ((n - t) >> 1)) >> (f.shift - 1);
+}
+
+// Page addressing of a window that starts at a known logical position.  For a
+// logical token t >= base, with rel = t - base (32-bit):
+//   slot   = (base_slot + (base_off + rel) / P) mod T
+//   offset = (base_off + rel) mod P
+struct PageMap {
+  int32_t base_slot;  // (base / P) mod T
+  int32_t base_off;   // base mod P
+};
+
+// ---------------------------------------------------------------- append
+struct AppendParams {
+  const void* k_new;      // [n][H][D]
+  const void* v_new;      // [n][H][D]
+  const float* ks_new;    // [n/P][H][nblk] or null
+  const float* vs_new;
+  void* k;                // [pages][H][P][D]
+  void* v;                // [pages][H][D][P]
+  float* ks;              // [pages][H][nblk]
+  float* vs;
+  int32_t n;              // tokens
+  int32_t H, D, P, T, nblk;
+  int32_t esize;          // bytes per element (4, 2, 1)
+  int32_t lead;           // (pos mod 64): index of the first token inside tile 0
+  PageMap map;            // for logical base = pos - lead (64-aligned)
+  FastDiv divP, divT;
+  int32_t table[WF_MAX_TABLE_LEN];
+};
+
+struct PoisonParams {
+  void* k;
+  void* v;
+  int32_t n, H, D, P, T;
+  int32_t esize;
+  PageMap map;  // base = first evicted token
+  FastDiv divP, divT;
+  int32_t table[WF_MAX_TABLE_LEN];
+};
+
+hipError_t launch_append(const AppendParams& p, int ntiles, hipStream_t s);
+hipError_t launch_poison(const PoisonParams& p, hipStream_t s);
+
+// ---------------------------------------------------------------- attention
+struct ChunkDesc {
+  int32_t q_begin;   // first query row
+  int32_t q_len;     // rows
+  int32_t ntiles;    // query tiles of this chunk
+  int32_t item0;     // first work item of this chunk
+  int32_t lead;      // kv_begin - tile origin (0..7): keys skipped in the first tile
+  int32_t nkeys;     // kv_end - kv_begin
+  PageMap map;       // for logical base = kv_begin - lead
+};
+
+struct AttnParams {
+  const void* q;     // [Nq][H][D]
+  void* o;           // [Nq][H][D]
+  float* lse;        // [H][Nq] or null
+  const void* k;     // cache pages
+  const void* v;
+  const float* ks;   // E4M3FN scales or null
+  const float* vs;
+  int32_t nq;        // total query rows
+  int32_t H, P, T, nblk;
+  float scale_log2;  // softmax scale * log2(e)
+  int32_t num_chunks;
+  int32_t num_items;
+  FastDiv divP, divT;
+  ChunkDesc chunk[WF_MAX_CHUNKS];
+  int32_t table[WF_MAX_TABLE_LEN];
+};
+
+// Query rows per workgroup of each instantiation (host needs it for the grid).
+constexpr int kBlockM = 128;
+
+hipError_t launch_attn_bf16(const AttnParams& p, int head_dim, hipStream_t s);
+hipError_t launch_attn_f32(const AttnParams& p, int head_dim, hipStream_t s);
+hipError_t launch_attn_fp8kv(const AttnParams& p, int head_dim, hipStream_t s);
+
+}  // namespace wf

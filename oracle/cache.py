@@ -148,18 +148,23 @@ class KVCacheModel:
             return z, z.copy()
         return np.concatenate(ks), np.concatenate(vs)
 
-    def gather(self, a, b):
-        """Values (float64) of logical tokens [a, b): K [b-a, H, D], V [b-a, H, D]."""
+    def gather(self, a, b, heads=None):
+        """Values (float64) of logical tokens [a, b): K [b-a, H', D], V [b-a, H', D].
+
+        heads optionally selects a subset of heads (H' = len(heads)); default all.
+        """
         kc, vc = self.gather_codes(a, b)
+        hs = np.arange(self.H) if heads is None else np.asarray(heads, dtype=np.int64)
+        kc, vc = kc[:, hs], vc[:, hs]
         if self.dtype == "f32":
             return decode_f32(kc), decode_f32(vc)
         if self.dtype == "bf16":
             return decode_bf16(kc), decode_bf16(vc)
         kd, vd = decode_e4m3fn(kc), decode_e4m3fn(vc)
-        ksc = np.empty((b - a, self.H), np.float64)
-        vsc = np.empty((b - a, self.H), np.float64)
+        ksc = np.empty((b - a, len(hs)), np.float64)
+        vsc = np.empty((b - a, len(hs)), np.float64)
         for t, page, off, cnt in self._runs(a, b):
             blk = (np.arange(off, off + cnt) // SCALE_BLOCK)
-            ksc[t - a:t - a + cnt] = self.k_scale[page][:, blk].T
-            vsc[t - a:t - a + cnt] = self.v_scale[page][:, blk].T
+            ksc[t - a:t - a + cnt] = self.k_scale[page][hs][:, blk].T
+            vsc[t - a:t - a + cnt] = self.v_scale[page][hs][:, blk].T
         return kd * ksc[:, :, None], vd * vsc[:, :, None]

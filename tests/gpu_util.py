@@ -1,0 +1,99 @@
+"""Helpers for the GPU parity tests: drive the HIP library and the oracle's
+cache model with the same seeded inputs, and measure the difference."""
+import numpy as np
+import torch
+
+import chunk_causal_dit_wf_amd as wf
+import oracle
+
+
+def dev(codes, dtype):
+    """Host storage codes -> device tensor in the library's storage dtype."""
+    if codes is None:
+        return None
+    a = np.ascontiguousarray(codes)
+    if dtype == "bf16":
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    if dtype == "scale":
+        return torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda()
+    return torch.from_numpy(a).cuda()
+
+
+def host_codes(t):
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def host_values(t):
+    c = host_codes(t)
+    if c.dtype == np.uint16:
+        return oracle.decode_bf16(c)
+    return c.astype(np.float64)
+
+
+def values_of(codes, dtype):
+    if dtype == "bf16":
+        return oracle.decode_bf16(codes)
+    return np.asarray(codes, np.float64)
+
+
+def random_pages(rng, shape, dtype):
+    """Finite random storage codes used to pre-fill pages (so unwritten rows are not zero)."""
+    if dtype == "f32":
+        return rng.standard_normal(shape, dtype=np.float32)
+    if dtype == "bf16":
+        return rng.integers(0, 1 << 15, size=shape, dtype=np.uint16) & np.uint16(0xBF7F)
+    return rng.integers(0, 0x7F, size=shape, dtype=np.uint8)
+
+
+class Pair:
+    """A device cache and the oracle's cache model, driven with identical operations."""
+
+    def __init__(self, num_pages, page_size, heads, dim, dtype, table, fill_seed=None):
+        self.dtype = dtype
+        kp = vp = None
+        if fill_seed is not None:
+            rng = np.random.default_rng(fill_seed)
+            kp = random_pages(rng, (num_pages, heads, page_size, dim), dtype)
+            vp = random_pages(rng, (num_pages, heads, dim, page_size), dtype)
+        self.ref = oracle.KVCacheModel(num_pages, page_size, heads, dim, dtype, table, k_pages=kp, v_pages=vp)
+        kt = dev(self.ref.k.copy(), dtype) if dtype != "fp8" else torch.from_numpy(self.ref.k.copy()).cuda()
+        vt = dev(self.ref.v.copy(), dtype) if dtype != "fp8" else torch.from_numpy(self.ref.v.copy()).cuda()
+        self.gpu = wf.KVCache(num_pages, page_size, heads, dim, dtype, list(table), k=kt, v=vt)
+
+    def append(self, pos, k, v, ks=None, vs=None):
+        d = "fp8" if self.dtype == "fp8" else self.dtype
+        wf.wf_kv_append(self.gpu, pos, dev(k, d), dev(v, d), dev(ks, "scale"), dev(vs, "scale"))
+        self.ref.append(pos, k, v, ks, vs)
+
+    def evict(self, n, poison=False):
+        wf.wf_kv_evict(self.gpu, n, poison=poison)
+        self.ref.evict(n, poison=poison)
+
+    def pages_equal(self):
+        torch.cuda.synchronize()
+        ok = np.array_equal(host_codes(self.gpu.k).view(np.uint8), self.ref.k.view(np.uint8)) and \
+            np.array_equal(host_codes(self.gpu.v).view(np.uint8), self.ref.v.view(np.uint8))
+        if self.dtype == "fp8":
+            ok = ok and np.array_equal(self.gpu.k_scale.cpu().numpy(), self.ref.k_scale) and \
+                np.array_equal(self.gpu.v_scale.cpu().numpy(), self.ref.v_scale)
+        return ok and (self.gpu.start, self.gpu.end) == (self.ref.start, self.ref.end)
+
+    def attend(self, q_dev, q_off, kb, ke, scale=0.0):
+        o, lse = wf.wf_chunk_attn_fwd(self.gpu, q_dev, q_off, kb, ke, scale, return_lse=True)
+        torch.cuda.synchronize()
+        return o, lse
+
+    def reference(self, q_vals, q_off, kb, ke, scale=None, heads=None):
+        """Oracle output for q_vals [Nq, H', D] (H' = len(heads) when a head subset is given)."""
+        a, b = int(min(kb)), int(max(ke))
+        K, V = self.ref.gather(a, b, heads=heads)
+        return oracle.chunk_attention(q_vals, K, V, q_off, kb, ke, scale=scale, kv_origin=a)
+
+
+def errors(got, ref):
+    d = np.abs(got - ref)
+    rel = np.sqrt((d ** 2).sum() / max((ref ** 2).sum(), 1e-300))
+    return float(d.max()), float(d.mean()), float(rel)

@@ -189,3 +189,15 @@ def test_cache_rejects_bad_operations():
     k8 = _codes(rng, 2, 1, 2, "fp8")
     with pytest.raises(ValueError):
         f.append(0, k8, k8, np.ones((0, 1, 1)), np.ones((0, 1, 1)))   # not page aligned
+
+
+def test_gather_head_subset_matches_full_gather():
+    rng = np.random.default_rng(7)
+    P, h, d = 128, 5, 3
+    c = KVCacheModel(3, P, h, d, "fp8", [2, 0, 1])
+    k, v = _codes(rng, 256, h, d, "fp8"), _codes(rng, 256, h, d, "fp8")
+    s = rng.uniform(0.5, 2, size=(2, h, 1)).astype(np.float32)
+    c.append(0, k, v, s, s * 2)
+    kf, vf = c.gather(10, 250)
+    ks, vs = c.gather(10, 250, heads=[4, 1])
+    assert np.array_equal(ks, kf[:, [4, 1]]) and np.array_equal(vs, vf[:, [4, 1]])
