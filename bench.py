@@ -1,0 +1,286 @@
+"""Benchmark: one forward round of chunk-causal attention over a rolling paged KV cache.
+
+A step is the whole hot path for one new chunk, once per layer:
+  evict the oldest chunk (once the 21-frame window is full) -> append the new
+  chunk's K/V (page scatter) -> chunk-causal attention of its 4680 query rows
+  over the 32760-key window.
+Default workload: Wan2.1-1.3B shape, 30 layers, 12 heads x 128, bf16, paged
+ring of 21 pages x 1560 tokens per layer (random page table per layer).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload round|call|wave|fp8round]
+
+Prints one JSON line.  Inputs are synthetic (seeded on the device) and already
+resident in HBM when the timed region starts.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+FP8_PEAK_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
+HBM_PEAK_GBPS = 8000.0
+FRAME = 1560
+CHUNK = 3 * FRAME
+WINDOW = 21 * FRAME
+METRIC = "chunk-attn TFLOP/s + % bf16 MFMA peak (1 GPU); KV-append GB/s; chunks/s"
+
+WORKLOADS = {
+    "round": dict(layers=30, H=12, D=128, dtype="bf16", std=0.5,
+                  name="wan1.3b forward round: 30 layers x (evict + append 4680 tok + attend 4680 q x 32760 k), "
+                       "H12 D128 bf16, paged ring P1560 T21"),
+    "fp8round": dict(layers=40, H=40, D=128, dtype="fp8", std=1.0,
+                     name="14b forward round: 40 layers x (evict + append 4680 tok + attend 4680 q x 32760 k), "
+                          "H40 D128 bf16 Q / e4m3 K,V, paged ring P1560 T21"),
+    "call": dict(layers=1, H=12, D=128, dtype="bf16", std=0.5,
+                 name="wan1.3b single call: 4680 q x 18720 k, H12 D128 bf16"),
+    "wave": dict(layers=1, H=12, D=128, dtype="bf16", std=0.5,
+                 name="wave: 4 chunks x 4680 q, prefixes 4680..18720, H12 D128 bf16"),
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="round", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=4680, help="query rows in the oracle timing sample")
+    return ap.parse_args()
+
+
+class Layer:
+    """One layer's cache plus the device inputs of its chunk."""
+
+    def __init__(self, wf, torch, synth, cfg, layer, gen):
+        H, D, dt = cfg["H"], cfg["D"], cfg["dtype"]
+        table = synth.permuted_table(synth.W_WAN_ROUND if dt == "bf16" else synth.W_14B_FP8, layer, 21)
+        self.cache = wf.KVCache(21, FRAME, H, D, dt, table.tolist(), device="cuda")
+        std = cfg["std"]
+        self.q = (torch.randn((CHUNK, H, D), generator=gen, device="cuda") * std).to(torch.bfloat16)
+        self.o = torch.empty_like(self.q)
+        if dt == "bf16":
+            self.k = (torch.randn((CHUNK, H, D), generator=gen, device="cuda") * std).to(torch.bfloat16)
+            self.v = (torch.randn((CHUNK, H, D), generator=gen, device="cuda") * std).to(torch.bfloat16)
+            self.ks = self.vs = None
+        else:
+            self.k, self.ks = quantize_dev(torch, torch.randn((CHUNK, H, D), generator=gen, device="cuda") * std)
+            self.v, self.vs = quantize_dev(torch, torch.randn((CHUNK, H, D), generator=gen, device="cuda") * std)
+
+
+def quantize_dev(torch, x):
+    """Synthetic E4M3FN pages: per (page, head, 128-token block) amax/448 scales (input preparation)."""
+    n, H, D = x.shape
+    pages = n // FRAME
+    nblk = -(-FRAME // 128)
+    xs = x.view(pages, FRAME, H, D)
+    pad = nblk * 128 - FRAME
+    xp = torch.nn.functional.pad(xs.abs(), (0, 0, 0, 0, 0, pad)).view(pages, nblk, 128, H, D)
+    amax = xp.amax(dim=(2, 4))                                  # [pages, nblk, H]
+    scale = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+    sc = scale.permute(0, 2, 1).contiguous()                    # [pages, H, nblk]
+    per_tok = scale.repeat_interleave(128, dim=1)[:, :FRAME]    # [pages, FRAME, H]
+    q = (xs / per_tok[..., None]).clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8)
+    return q.view(n, H, D).contiguous(), sc
+
+
+def attn_flops(H, D, rows, keys):
+    return 4.0 * D * H * rows * keys
+
+
+def run_round(args, cfg):
+    import torch
+    import chunk_causal_dit_wf_amd as wf
+    import synth
+
+    wf.lib()
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(synth.SEED)
+    layers = [Layer(wf, torch, synth, cfg, l, gen) for l in range(cfg["layers"])]
+    H, D = cfg["H"], cfg["D"]
+    # prefill 18 frames (6 chunks) per layer with the layer's chunk data
+    for L in layers:
+        for c in range(6):
+            wf.wf_kv_append(L.cache, c * CHUNK, L.k, L.v, L.ks, L.vs)
+    torch.cuda.synchronize()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def step(record):
+        marks = []
+        for L in layers:
+            c = L.cache
+            if c.end - c.start + CHUNK > c.capacity:
+                wf.wf_kv_evict(c, CHUNK)
+            e0 = ev() if record else None
+            if record:
+                e0.record()
+            wf.wf_kv_append(c, c.end, L.k, L.v, L.ks, L.vs)
+            e1 = ev() if record else None
+            if record:
+                e1.record()
+            kb = max(c.start, c.end - WINDOW)
+            wf.wf_chunk_attn_fwd(c, L.q, [0, CHUNK], [kb], [c.end], o=L.o)
+            if record:
+                e2 = ev()
+                e2.record()
+                marks.append((e0, e1, e2, c.end - kb))
+        return marks
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t_start, t_end = ev(), ev()
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record()
+    all_marks = []
+    for _ in range(args.steps):
+        all_marks += step(True)
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    app_ms = [a.elapsed_time(b) for a, b, _, _ in all_marks]
+    att_ms = [b.elapsed_time(c) for _, b, c, _ in all_marks]
+    keys = [k for _, _, _, k in all_marks]
+    flops_per_launch = attn_flops(H, D, CHUNK, keys[0])
+    assert all(k == WINDOW for k in keys)
+    esize = 2 if cfg["dtype"] == "bf16" else 1
+    app_bytes = 2 * 2 * CHUNK * H * D * esize
+    if cfg["dtype"] == "fp8":
+        app_bytes += 2 * 2 * (CHUNK // FRAME) * H * (-(-FRAME // 128)) * 4
+    total_flops = flops_per_launch * len(att_ms)
+    ms_step = total_ms / args.steps
+    avg_att = sum(att_ms) / len(att_ms)
+    avg_app = sum(app_ms) / len(app_ms)
+    return dict(
+        ms_per_step=ms_step, wall_s=wall, value=total_flops / (total_ms * 1e-3) / 1e12,
+        attn_kernel_ms=avg_att, attn_tflops=flops_per_launch / (avg_att * 1e-3) / 1e12,
+        append_kernel_ms=avg_app, append_gbps=app_bytes / (avg_app * 1e-3) / 1e9,
+        chunks_per_s=1000.0 / ms_step, flops_per_launch=flops_per_launch, append_bytes=app_bytes,
+        H=H, D=D, layers=cfg["layers"])
+
+
+def run_single(args, cfg, wave):
+    import torch
+    import chunk_causal_dit_wf_amd as wf
+    import synth
+
+    wf.lib()
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(synth.SEED)
+    H, D = cfg["H"], cfg["D"]
+    cache = wf.KVCache(12, FRAME, H, D, "bf16", list(range(12)), device="cuda")
+    for c in range(4):
+        k = (torch.randn((CHUNK, H, D), generator=gen, device="cuda") * 0.5).to(torch.bfloat16)
+        wf.wf_kv_append(cache, c * CHUNK, k, k.clone())
+    rows = 4 * CHUNK if wave else CHUNK
+    q = (torch.randn((rows, H, D), generator=gen, device="cuda") * 0.5).to(torch.bfloat16)
+    o = torch.empty_like(q)
+    if wave:
+        q_off, kb, ke = [0, CHUNK, 2 * CHUNK, 3 * CHUNK, 4 * CHUNK], [0] * 4, [CHUNK * (j + 1) for j in range(4)]
+        flops = sum(attn_flops(H, D, CHUNK, e) for e in ke)
+    else:
+        q_off, kb, ke = [0, CHUNK], [0], [4 * CHUNK]
+        flops = attn_flops(H, D, CHUNK, 4 * CHUNK)
+    for _ in range(args.warmup):
+        wf.wf_chunk_attn_fwd(cache, q, q_off, kb, ke, o=o)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for a, b in evs:
+        a.record()
+        wf.wf_chunk_attn_fwd(cache, q, q_off, kb, ke, o=o)
+        b.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = [a.elapsed_time(b) for a, b in evs]
+    avg = sum(ms) / len(ms)
+    return dict(ms_per_step=avg, wall_s=wall, value=flops / (avg * 1e-3) / 1e12, attn_kernel_ms=avg,
+                attn_tflops=flops / (avg * 1e-3) / 1e12, flops_per_launch=flops, H=H, D=D, layers=1,
+                append_kernel_ms=None, append_gbps=None, chunks_per_s=None, append_bytes=None)
+
+
+def cpu_baseline(rows, H, D, keys):
+    """Time the float64 oracle on the host for one layer's attention (rows x keys x H)."""
+    import numpy as np
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    rng = np.random.default_rng(42)
+    q = rng.standard_normal((rows, H, D)) * 0.5
+    k = rng.standard_normal((keys, H, D)) * 0.5
+    v = rng.standard_normal((keys, H, D)) * 0.5
+    t0 = time.perf_counter()
+    oracle.chunk_attention(q, k, v, [0, rows], [0], [keys])
+    dt = time.perf_counter() - t0
+    return dict(value=attn_flops(H, D, rows, keys) / dt / 1e12, unit="TFLOP/s", cores=threads, kind="oracle",
+                sample="float64 oracle, one layer's attention: %d query rows x %d keys x %d heads x D%d (%.1f s)"
+                       % (rows, keys, H, D, dt))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on exactly one GPU: multi-GPU runs are not part of this build "
+              "(requested --gpus %d)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    cfg = WORKLOADS[args.workload]
+    if args.workload in ("round", "fp8round"):
+        r = run_round(args, cfg)
+    else:
+        r = run_single(args, cfg, wave=args.workload == "wave")
+    peak = FP8_PEAK_TFLOPS if cfg["dtype"] == "fp8" else BF16_PEAK_TFLOPS
+    out = {
+        "metric": METRIC,
+        "value": round(r["value"], 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg["dtype"] == "bf16" else "bf16 Q / e4m3 K,V",
+        "data": "synthetic (seeded N(0, s^2) on device, random page tables)",
+        "config": {"workload": cfg["name"], "layers": cfg["layers"], "heads": r["H"], "head_dim": r["D"],
+                   "query_rows": CHUNK, "keys": WINDOW if "round" in args.workload else None,
+                   "parallelism": "single GPU"},
+        "pct_bf16_peak": round(100.0 * r["value"] / BF16_PEAK_TFLOPS, 2),
+        "attn_kernel_tflops": round(r["attn_tflops"], 2),
+        "attn_kernel_ms": round(r["attn_kernel_ms"], 4),
+        "kv_append_GBps": None if r["append_gbps"] is None else round(r["append_gbps"], 1),
+        "append_kernel_ms": None if r["append_kernel_ms"] is None else round(r["append_kernel_ms"], 5),
+        "chunks_per_s": None if r["chunks_per_s"] is None else round(r["chunks_per_s"], 3),
+        "roofline": {"bound": "mfma", "achieved": round(r["attn_tflops"], 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(r["attn_tflops"] / peak, 4), "traffic": None,
+                     "kernel": "attn_fwd_bf16_kernel<128,%s>" % ("true" if cfg["dtype"] == "fp8" else "false"),
+                     "flops_per_launch": r["flops_per_launch"]},
+    }
+    if r["append_gbps"] is not None:
+        out["append_roofline"] = {"bound": "hbm", "achieved": round(r["append_gbps"], 1), "peak": HBM_PEAK_GBPS,
+                                  "unit": "GB/s", "frac": round(r["append_gbps"] / HBM_PEAK_GBPS, 4),
+                                  "bytes_per_launch": r["append_bytes"]}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(min(args.cpu_rows, CHUNK), r["H"], r["D"],
+                                           WINDOW if "round" in args.workload else 4 * CHUNK)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
