@@ -27,6 +27,8 @@
 //
 // Roofline: dense MFMA.  Algorithmic flops per visible (query, key) pair and
 // head are 4 * head_dim (2 for Q K^T, 2 for P V).
+#include <type_traits>
+
 #include "wf_internal.h"
 
 namespace wf {
@@ -85,89 +87,147 @@ __device__ __forceinline__ Item decode_item(const AttnParams& p, int item) {
 
 // ---------------------------------------------------------------------------
 // bf16 Q (and bf16 or E4M3FN K/V) kernel.
-// LDS per stage: K tile [64 keys][D] bf16, 16-byte chunks XOR-swizzled by
-// (key & 7); V^T tile [D][64 keys] bf16, 16-byte chunks XOR-swizzled by
-// (d & 7), keys permuted inside 16-key groups.
+//
+// LDS holds two K tiles and two V^T tiles (bf16).  Rows are padded by 16
+// bytes (K: 64 keys x (2D+16) B; V^T: D dims x (128+16) B) so that the 8 (or
+// 16) lanes an LDS cycle serves hit distinct banks and every fragment access
+// is a fixed immediate offset from one per-lane base address.  Inside each
+// 16-key group of a V^T row the keys are stored in the order the P^T operand
+// consumes them (bits 2 and 3 of the key index swapped).
+//
+// Software pipeline (one barrier per 64-key tile).  Iteration j:
+//   issue global loads of K[j+2] and V[j+1];
+//   S[j+1] = K[j+1] Q^T  (MFMA, independent of ...)
+//   softmax(S[j]) -> P[j] (VALU), so the two interleave;
+//   O^T += V^T[j] P^T[j] (MFMA);
+//   write K[j+2], V[j+1] into the LDS buffers freed by iteration j-1.
 // ---------------------------------------------------------------------------
 template <int D, bool FP8KV>
-struct TileLoader {
-  static constexpr int KCH = D / 8;                 // 16-byte bf16 chunks per K row in LDS
-  static constexpr int KITEMS = BN * KCH / NT;      // K chunks per thread
-  static constexpr int VITEMS = D * (BN / 8) / NT;  // V 8-key groups per thread
-  static constexpr int KBYTES = BN * D * 2;
-  static constexpr int STAGE = KBYTES + D * BN * 2;
-  // staged registers: bf16 payload (16 B per item) or raw fp8 (8 B per item) + scale
-  uint4 kr[KITEMS];
-  uint4 vr[VITEMS];
-  float ksc[KITEMS];
-  float vsc[VITEMS];
-  uint32_t kmask;  // bit i: K item i valid
-  uint32_t vfull;  // bit i: V group i fully valid
-  uint32_t vpart;  // bit i: V group i partially valid (element masks below)
-  uint8_t vmask[VITEMS];
+struct Geo {
+  static constexpr int ESZ = FP8KV ? 1 : 2;       // cache bytes per element
+  static constexpr int KROW = 2 * D + 16;         // LDS bytes per K row
+  static constexpr int KTILE = BN * KROW;
+  static constexpr int VROW = 2 * BN + 16;        // LDS bytes per V^T row
+  static constexpr int VTILE = D * VROW;
+  static constexpr int LDS = 2 * KTILE + 2 * VTILE;
+  static constexpr int KCH = D / 8;               // 8-element chunks per K row
+  static constexpr int KPASS = NT / KCH;          // keys per loader pass
+  static constexpr int KITEMS = BN / KPASS;       // K chunks per thread
+  static constexpr int VPASS = NT / 8;            // V^T rows per loader pass
+  static constexpr int VITEMS = D / VPASS;        // V 8-key groups per thread
 };
 
-template <int D, bool FP8KV>
-__device__ __forceinline__ void load_tile(TileLoader<D, FP8KV>& L, const AttnParams& p,
-                                          const ChunkDesc& cd, const int32_t* table, int head,
-                                          int j) {
-  using TL = TileLoader<D, FP8KV>;
-  const int tid = threadIdx.x;
-  const int lo = cd.lead, hi = cd.lead + cd.nkeys;
-  const int rel0 = j * BN;
-  // tile start page/offset (uniform)
+// Register staging of one tile's K (or V) slice owned by this thread.
+template <int N>
+struct Stage {
+  uint4 w[N];    // bf16 payload, or E4M3FN codes in .x/.y
+  float sc[N];   // E4M3FN block scale (1 otherwise)
+  uint8_t m[N];  // per-element validity (8 keys / 8 dims); 0xFF = all valid
+};
+
+// Per-tile page geometry (uniform): page and offset of the tile's first key.
+struct TilePos {
   int32_t page0, off0;
-  locate(cd.map, p.divP, p.divT, table, (uint32_t)rel0, page0, off0);
-  L.kmask = 0;
+  bool fast;  // all keys valid and inside one page
+};
+
+__device__ __forceinline__ TilePos tile_pos(const AttnParams& p, const ChunkDesc& cd, const int32_t* table,
+                                            int t) {
+  TilePos tp;
+  const int rel0 = t * BN;
+  locate(cd.map, p.divP, p.divT, table, (uint32_t)rel0, tp.page0, tp.off0);
+  tp.fast = rel0 >= cd.lead && rel0 + BN <= cd.lead + cd.nkeys && tp.off0 + BN <= p.P;
+  return tp;
+}
+
+template <int D, bool FP8KV>
+__device__ __forceinline__ void load_k(Stage<Geo<D, FP8KV>::KITEMS>& st, const AttnParams& p,
+                                       const ChunkDesc& cd, const int32_t* table, int head, int t) {
+  using G = Geo<D, FP8KV>;
+  const int tid = threadIdx.x;
+  const int kq = tid / G::KCH, ch = tid - kq * G::KCH;
+  const TilePos tp = tile_pos(p, cd, table, t);
+  const uint8_t* kb = (const uint8_t*)p.k;
+  if (tp.fast) {
+    const uint8_t* base = kb + (((int64_t)tp.page0 * p.H + head) * p.P + tp.off0) * (D * G::ESZ);
+    const int64_t sbase = ((int64_t)tp.page0 * p.H + head) * p.nblk;
 #pragma unroll
-  for (int r = 0; r < TL::KITEMS; ++r) {
-    const int idx = tid + NT * r;
-    const int key = idx / TL::KCH, ch = idx - key * TL::KCH;
-    const int rel = rel0 + key;
-    L.kr[r] = make_uint4(0, 0, 0, 0);
-    L.ksc[r] = 1.f;
+    for (int r = 0; r < G::KITEMS; ++r) {
+      const int key = kq + r * G::KPASS;
+      const uint8_t* a = base + key * (D * G::ESZ) + ch * (8 * G::ESZ);
+      if constexpr (FP8KV) {
+        const uint2 raw = *(const uint2*)a;
+        st.w[r] = make_uint4(raw.x, raw.y, 0, 0);
+        st.sc[r] = p.ks[sbase + ((tp.off0 + key) >> 7)];
+      } else {
+        st.w[r] = *(const uint4*)a;
+        st.sc[r] = 1.f;
+      }
+      st.m[r] = 0xFF;
+    }
+    return;
+  }
+  const int lo = cd.lead, hi = cd.lead + cd.nkeys;
+#pragma unroll
+  for (int r = 0; r < G::KITEMS; ++r) {
+    const int key = kq + r * G::KPASS;
+    const int rel = t * BN + key;
+    st.w[r] = make_uint4(0, 0, 0, 0);
+    st.sc[r] = 1.f;
+    st.m[r] = 0;
     if (rel >= lo && rel < hi) {
-      int32_t page = page0, off = off0 + key;
+      int32_t page = tp.page0, off = tp.off0 + key;
       if (off >= p.P) locate(cd.map, p.divP, p.divT, table, (uint32_t)rel, page, off);
       const int64_t row = ((int64_t)page * p.H + head) * p.P + off;
+      const uint8_t* a = kb + row * (D * G::ESZ) + ch * (8 * G::ESZ);
       if constexpr (FP8KV) {
-        const uint2 raw = *(const uint2*)((const uint8_t*)p.k + row * D + ch * 8);
-        L.kr[r] = make_uint4(raw.x, raw.y, 0, 0);
-        L.ksc[r] = p.ks[((int64_t)page * p.H + head) * p.nblk + (off >> 7)];
+        const uint2 raw = *(const uint2*)a;
+        st.w[r] = make_uint4(raw.x, raw.y, 0, 0);
+        st.sc[r] = p.ks[((int64_t)page * p.H + head) * p.nblk + (off >> 7)];
       } else {
-        L.kr[r] = *(const uint4*)((const __bf16*)p.k + row * D + ch * 8);
+        st.w[r] = *(const uint4*)a;
       }
-      L.kmask |= 1u << r;
+      st.m[r] = 0xFF;
     }
   }
-  L.vfull = 0;
-  L.vpart = 0;
+}
+
+template <int D, bool FP8KV>
+__device__ __forceinline__ void load_v(Stage<Geo<D, FP8KV>::VITEMS>& st, const AttnParams& p,
+                                       const ChunkDesc& cd, const int32_t* table, int head, int t) {
+  using G = Geo<D, FP8KV>;
+  const int tid = threadIdx.x;
+  const int vd = tid >> 3, a8 = tid & 7;
+  const TilePos tp = tile_pos(p, cd, table, t);
+  const uint8_t* vb = (const uint8_t*)p.v;
+  const int rel = t * BN + 8 * a8;
+  int32_t page = tp.page0, off = tp.off0 + 8 * a8;
+  uint8_t m = 0xFF;
+  if (!tp.fast) {
+    const int lo = cd.lead, hi = cd.lead + cd.nkeys;
+    m = 0;
 #pragma unroll
-  for (int r = 0; r < TL::VITEMS; ++r) {
-    const int idx = tid + NT * r;
-    const int d = idx >> 3, a = idx & 7;
-    const int rel = rel0 + 8 * a;
-    L.vr[r] = make_uint4(0, 0, 0, 0);
-    L.vsc[r] = 1.f;
-    L.vmask[r] = 0;
-    if (rel + 8 > lo && rel < hi) {
-      int32_t page = page0, off = off0 + 8 * a;
-      if (off >= p.P) locate(cd.map, p.divP, p.divT, table, (uint32_t)rel, page, off);
-      const int64_t col = (((int64_t)page * p.H + head) * D + d) * p.P + off;
+    for (int e = 0; e < 8; ++e) m |= (uint8_t)((rel + e >= lo && rel + e < hi) ? 1u << e : 0u);
+    if (off >= p.P) locate(cd.map, p.divP, p.divT, table, (uint32_t)rel, page, off);
+  }
+  const uint8_t* base = vb + (((int64_t)page * p.H + head) * D * p.P + off) * G::ESZ;
+  float sc = 1.f;
+  if constexpr (FP8KV) {
+    if (m) sc = p.vs[((int64_t)page * p.H + head) * p.nblk + (off >> 7)];
+  }
+#pragma unroll
+  for (int r = 0; r < G::VITEMS; ++r) {
+    const int d = vd + r * G::VPASS;
+    st.w[r] = make_uint4(0, 0, 0, 0);
+    st.sc[r] = sc;
+    st.m[r] = m;
+    if (m) {
+      const uint8_t* a = base + (int64_t)d * p.P * G::ESZ;
       if constexpr (FP8KV) {
-        const uint2 raw = *(const uint2*)((const uint8_t*)p.v + col);
-        L.vr[r] = make_uint4(raw.x, raw.y, 0, 0);
-        L.vsc[r] = p.vs[((int64_t)page * p.H + head) * p.nblk + (off >> 7)];
+        const uint2 raw = *(const uint2*)a;
+        st.w[r] = make_uint4(raw.x, raw.y, 0, 0);
       } else {
-        L.vr[r] = *(const uint4*)((const __bf16*)p.v + col);
-      }
-      if (rel >= lo && rel + 8 <= hi) {
-        L.vfull |= 1u << r;
-      } else {
-        uint8_t m = 0;
-        for (int e = 0; e < 8; ++e) m |= (uint8_t)((rel + e >= lo && rel + e < hi) ? 1u << e : 0u);
-        L.vmask[r] = m;
-        L.vpart |= 1u << r;
+        st.w[r] = *(const uint4*)a;
       }
     }
   }
@@ -188,172 +248,219 @@ __device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint4 raw, float scale) {
                     pack_bf16x2(__builtin_amdgcn_cvt_scalef32_pk_f32_fp8(raw.y, 1.0f, false), scale),
                     pack_bf16x2(__builtin_amdgcn_cvt_scalef32_pk_f32_fp8(raw.y, 1.0f, true), scale));
 }
+__device__ __forceinline__ uint4 mask_bf16x8(uint4 v, uint32_t m) {
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    if (!((m >> e) & 1u)) w[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
 
 template <int D, bool FP8KV>
-__device__ __forceinline__ void store_tile(const TileLoader<D, FP8KV>& L, char* stage) {
-  using TL = TileLoader<D, FP8KV>;
+__device__ __forceinline__ void store_k(const Stage<Geo<D, FP8KV>::KITEMS>& st, char* kbuf) {
+  using G = Geo<D, FP8KV>;
   const int tid = threadIdx.x;
+  const int kq = tid / G::KCH, ch = tid - kq * G::KCH;
+  char* base = kbuf + kq * G::KROW + ch * 16;
 #pragma unroll
-  for (int r = 0; r < TL::KITEMS; ++r) {
-    const int idx = tid + NT * r;
-    const int key = idx / TL::KCH, ch = idx - key * TL::KCH;
-    uint4 v = L.kr[r];
-    if constexpr (FP8KV) v = fp8x8_to_bf16x8(v, L.ksc[r]);
-    *(uint4*)(stage + key * (D * 2) + ((ch ^ (key & 7)) << 4)) = v;
-  }
-  char* vt = stage + TL::KBYTES;
-#pragma unroll
-  for (int r = 0; r < TL::VITEMS; ++r) {
-    const int idx = tid + NT * r;
-    const int d = idx >> 3, a = idx & 7;
-    uint4 v = L.vr[r];
-    if constexpr (FP8KV) v = fp8x8_to_bf16x8(v, L.vsc[r]);
-    if ((L.vpart >> r) & 1u) {
-      const uint32_t m = L.vmask[r];
-      uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (!((m >> e) & 1u)) w[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
-      v = make_uint4(w[0], w[1], w[2], w[3]);
-    }
-    // keys 8a..8a+3 -> chunk (a & ~1), keys 8a+4..8a+7 -> chunk (a | 1); byte offset 8*(a & 1)
-    const int sw = d & 7;
-    char* row = vt + d * (BN * 2) + ((a & 1) << 3);
-    *(uint2*)(row + (((a & ~1) ^ sw) << 4)) = make_uint2(v.x, v.y);
-    *(uint2*)(row + (((a | 1) ^ sw) << 4)) = make_uint2(v.z, v.w);
+  for (int r = 0; r < G::KITEMS; ++r) {
+    uint4 v = st.w[r];
+    if constexpr (FP8KV) v = fp8x8_to_bf16x8(v, st.sc[r]);
+    *(uint4*)(base + r * G::KPASS * G::KROW) = v;
   }
 }
 
 template <int D, bool FP8KV>
+__device__ __forceinline__ void store_v(const Stage<Geo<D, FP8KV>::VITEMS>& st, char* vbuf) {
+  using G = Geo<D, FP8KV>;
+  const int tid = threadIdx.x;
+  const int vd = tid >> 3, a8 = tid & 7;
+  // keys 8a..8a+3 -> 16-byte chunk (a & ~1), keys 8a+4..8a+7 -> chunk (a | 1); byte 8*(a & 1)
+  char* base = vbuf + vd * G::VROW + ((a8 & ~1) << 4) + ((a8 & 1) << 3);
+#pragma unroll
+  for (int r = 0; r < G::VITEMS; ++r) {
+    uint4 v = st.w[r];
+    if constexpr (FP8KV) v = fp8x8_to_bf16x8(v, st.sc[r]);
+    if (st.m[r] != 0xFF) v = mask_bf16x8(v, st.m[r]);
+    char* row = base + r * G::VPASS * G::VROW;
+    *(uint2*)row = make_uint2(v.x, v.y);
+    *(uint2*)(row + 16) = make_uint2(v.z, v.w);
+  }
+}
+
+template <int D, bool FP8KV>
+__device__ __forceinline__ void qk_tile(f32x16 (&s)[2], const char* kbuf, const bf16x8 (&qf)[D / 16],
+                                        int lane_off) {
+  using G = Geo<D, FP8KV>;
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[b][i] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const bf16x8 kf = *(const bf16x8*)(kbuf + lane_off + b * 32 * G::KROW + ks * 32);
+      s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[b], 0, 0, 0);
+    }
+  }
+}
+
+constexpr float kRescaleThreshold = 8.0f;  // log2 units: p <= 2^8 between rescales
+
+template <int D>
+__device__ __forceinline__ void softmax_tile(f32x16 (&s)[2], bf16x8 (&pf)[2][2], f32x16 (&o)[D / 32], float& m,
+                                             float& l, float scale_log2, int rel0, int lo, int hi, int hf) {
+  if (rel0 < lo || rel0 + BN > hi) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int rel = rel0 + b * 32 + 8 * (i >> 2) + 4 * hf + (i & 3);
+        if (rel < lo || rel >= hi) s[b][i] = -INFINITY;
+      }
+  }
+  float mx = fmaxf(s[0][0], s[0][1]);
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[b][i]);
+  mx = half_max(mx) * scale_log2;
+  // Exact lazy rescaling: the reference point m only moves when the running
+  // maximum exceeds it by more than the threshold; O and l always share m.
+  if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleThreshold) != 0) {
+    const float m_new = fmaxf(m, mx);
+    const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+    m = m_new;
+    l *= alpha;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+  }
+  const float nm = -m;
+  typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+  const bf16x2v ones = {(__bf16)1.0f, (__bf16)1.0f};
+  float l0 = 0.f, l1 = 0.f;
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int r = 0; r < 8; r += 2) {
+        const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][8 * u + r], scale_log2, nm));
+        const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][8 * u + r + 1], scale_log2, nm));
+        const bf16x2v pk = {(__bf16)e0, (__bf16)e1};
+        pf[b][u][r] = pk[0];
+        pf[b][u][r + 1] = pk[1];
+        if (r & 2)
+          l1 = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, l1, false);
+        else
+          l0 = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, l0, false);
+      }
+  l += l0 + l1;
+}
+
+template <int D, bool FP8KV>
+__device__ __forceinline__ void pv_tile(f32x16 (&o)[D / 32], const char* vbuf, const bf16x8 (&pf)[2][2],
+                                        int lane_off) {
+  using G = Geo<D, FP8KV>;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const bf16x8 vf = *(const bf16x8*)(vbuf + lane_off + db * 32 * G::VROW + (4 * b + 2 * u) * 16);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[b][u], o[db], 0, 0, 0);
+      }
+}
+
+template <int D, bool FP8KV>
 __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(const AttnParams p) {
-  using TL = TileLoader<D, FP8KV>;
-  constexpr int KS = D / 16;   // MFMA k-steps over the head dim
-  constexpr int DB = D / 32;   // 32-row blocks of O^T
+  using G = Geo<D, FP8KV>;
+  constexpr int KS = D / 16;
+  constexpr int DB = D / 32;
   extern __shared__ __align__(16) char smem[];
   __shared__ int32_t table[WF_MAX_TABLE_LEN];
+  char* kbuf0 = smem;
+  char* kbuf1 = smem + G::KTILE;
+  char* vbuf0 = smem + 2 * G::KTILE;
+  char* vbuf1 = vbuf0 + G::VTILE;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int lq = lane & 31;     // query column owned by this lane
-  const int hf = lane >> 5;     // 32-lane half
+  const int lq = lane & 31;  // query column owned by this lane
+  const int hf = lane >> 5;  // 32-lane half
 
   for (int i = tid; i < p.T; i += NT) table[i] = p.table[i];
 
   const Item it = decode_item(p, blockIdx.x);
   const ChunkDesc cd = p.chunk[it.c];
   const int head = it.head;
-  const int row = cd.q_begin + it.qt * BM + wave * 32 + lq;  // this lane's query row
-  const bool row_ok = (it.qt * BM + wave * 32 + lq) < cd.q_len;
-  const int nt = (cd.lead + cd.nkeys + BN - 1) / BN;
+  const int qrow = it.qt * BM + wave * 32 + lq;
+  const int row = cd.q_begin + qrow;
+  const bool row_ok = qrow < cd.q_len;
+  const int lo = cd.lead, hi = cd.lead + cd.nkeys;
+  const int nt = (hi + BN - 1) / BN;
+  const int k_lane = lq * G::KROW + hf * 16;
+  const int v_lane = lq * G::VROW + hf * 16;
 
-  // Q^T fragments (B operand): lane holds 8 consecutive dims of its row per k-step.
   bf16x8 qf[KS];
   {
-    const __bf16* qrow = (const __bf16*)p.q + ((int64_t)row * p.H + head) * D;
+    const __bf16* qp = (const __bf16*)p.q + ((int64_t)row * p.H + head) * D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       uint4 v = make_uint4(0, 0, 0, 0);
-      if (row_ok) v = *(const uint4*)(qrow + ks * 16 + hf * 8);
+      if (row_ok) v = *(const uint4*)(qp + ks * 16 + hf * 8);
       qf[ks] = __builtin_bit_cast(bf16x8, v);
     }
   }
-
   f32x16 o[DB];
 #pragma unroll
   for (int b = 0; b < DB; ++b)
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[b][i] = 0.f;
-  float m = -INFINITY;  // running max, log2 domain
-  float l = 0.f;        // running partial sum over this lane's keys
+  float m = -INFINITY, l = 0.f;
 
-  __syncthreads();  // page table in LDS
-  TL L;
-  load_tile<D, FP8KV>(L, p, cd, table, head, 0);
-  store_tile<D, FP8KV>(L, smem);
+  __syncthreads();  // page table
+  Stage<G::KITEMS> sk;
+  Stage<G::VITEMS> sv;
+  load_k<D, FP8KV>(sk, p, cd, table, head, 0);
+  load_v<D, FP8KV>(sv, p, cd, table, head, 0);
+  store_k<D, FP8KV>(sk, kbuf0);
+  store_v<D, FP8KV>(sv, vbuf0);
+  if (nt > 1) {
+    load_k<D, FP8KV>(sk, p, cd, table, head, 1);
+    store_k<D, FP8KV>(sk, kbuf1);
+  }
   __syncthreads();
 
-  for (int j = 0; j < nt; ++j) {
-    char* stage = smem + (j & 1) * TL::STAGE;
-    if (j + 1 < nt) load_tile<D, FP8KV>(L, p, cd, table, head, j + 1);
+  f32x16 sa[2], sb[2];
+  bf16x8 pf[2][2];
+  qk_tile<D, FP8KV>(sa, kbuf0, qf, k_lane);
 
-    // ---- S^T = K Q^T for two 32-key blocks
-    f32x16 s[2];
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s[b][i] = 0.f;
-      const int key = b * 32 + lq;
-      const char* krow = stage + key * (D * 2);
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int ch = (2 * ks + hf) ^ (key & 7);
-        const bf16x8 kf = *(const bf16x8*)(krow + (ch << 4));
-        s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[b], 0, 0, 0);
-      }
-    }
-
-    // ---- mask keys outside [lead, lead + nkeys) (first / last tile only)
-    const int rel0 = j * BN;
-    if (rel0 < cd.lead || rel0 + BN > cd.lead + cd.nkeys) {
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int rel = rel0 + b * 32 + 8 * (i >> 2) + 4 * hf + (i & 3);
-          if (rel < cd.lead || rel >= cd.lead + cd.nkeys) s[b][i] = -INFINITY;
-        }
-    }
-
-    // ---- online softmax (log2 domain)
-    float mx = s[0][0];
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[b][i]);
-    mx = half_max(mx);
-    const float m_new = fmaxf(m, mx * p.scale_log2);
-    const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-    m = m_new;
-    float rs = 0.f;
-    bf16x8 pf[2][2];
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][8 * u + r], p.scale_log2, -m_new));
-          rs += e;
-          pf[b][u][r] = (__bf16)e;
-        }
-    l = l * alpha + rs;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
-
-    // ---- O^T += V^T P^T
-    const char* vt = stage + TL::KBYTES;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const int d = db * 32 + lq;
-      const char* vrow = vt + d * (BN * 2);
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int ch = (4 * b + 2 * u + hf) ^ (d & 7);
-          const bf16x8 vf = *(const bf16x8*)(vrow + (ch << 4));
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[b][u], o[db], 0, 0, 0);
-        }
-    }
-
-    if (j + 1 < nt) store_tile<D, FP8KV>(L, smem + ((j + 1) & 1) * TL::STAGE);
+  // One pipeline step; `even` selects the buffer parity at compile time.
+  auto step = [&](auto even_tag, f32x16(&s_cur)[2], f32x16(&s_next)[2], int j) {
+    constexpr bool even = decltype(even_tag)::value;
+    char* kb_next = even ? kbuf1 : kbuf0;  // holds K[j+1]
+    char* kb_free = even ? kbuf0 : kbuf1;  // receives K[j+2]
+    char* vb_cur = even ? vbuf0 : vbuf1;   // holds V[j]
+    char* vb_free = even ? vbuf1 : vbuf0;  // receives V[j+1]
+    const bool has1 = j + 1 < nt, has2 = j + 2 < nt;
+    if (has2) load_k<D, FP8KV>(sk, p, cd, table, head, j + 2);
+    if (has1) load_v<D, FP8KV>(sv, p, cd, table, head, j + 1);
+    if (has1) qk_tile<D, FP8KV>(s_next, kb_next, qf, k_lane);
+    softmax_tile<D>(s_cur, pf, o, m, l, p.scale_log2, j * BN, lo, hi, hf);
+    pv_tile<D, FP8KV>(o, vb_cur, pf, v_lane);
+    if (has2) store_k<D, FP8KV>(sk, kb_free);
+    if (has1) store_v<D, FP8KV>(sv, vb_free);
     __syncthreads();
+  };
+  for (int j = 0; j < nt; j += 2) {
+    step(std::true_type{}, sa, sb, j);
+    if (j + 1 < nt) step(std::false_type{}, sb, sa, j + 1);
   }
 
-  // ---- epilogue: O = O^T / l, lse = (m + log2 l) ln 2
   const float lt = half_sum(l);
   const float inv = 1.f / lt;
   if (row_ok) {
@@ -497,8 +604,7 @@ __global__ __launch_bounds__(NT) void attn_fwd_f32_kernel(const AttnParams p) {
 
 template <int D, bool FP8KV>
 hipError_t launch_bf16_t(const AttnParams& p, hipStream_t s) {
-  using TL = TileLoader<D, FP8KV>;
-  const size_t lds = 2 * TL::STAGE;
+  const size_t lds = Geo<D, FP8KV>::LDS;
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(&attn_fwd_bf16_kernel<D, FP8KV>),
       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
