@@ -289,6 +289,10 @@ wf_status wf_chunk_attn_fwd(const wf_kv_cache* c, const void* q, int32_t q_dtype
   p.divP = wf::make_fastdiv((uint32_t)c->page_size);
   p.divT = wf::make_fastdiv((uint32_t)c->table_len);
   std::memcpy(p.table, c->page_table, sizeof(int32_t) * c->table_len);
+  // The DMA kernel addresses a key tile as at most two page runs with 32-bit
+  // byte offsets: it takes bf16 caches with pages of at least one tile (64
+  // keys) and under 4 GiB.  Everything else goes to the register-staged kernel.
+  const bool use_dma = kvd == WF_BF16 && c->page_size >= 64 && kvb < ((uint64_t)1 << 32);
 
   // Longest-processing-time-first order: chunks with the most (query x key) work are issued first.
   std::vector<int> order;
@@ -299,13 +303,14 @@ wf_status wf_chunk_attn_fwd(const wf_kv_cache* c, const void* q, int32_t q_dtype
     const int64_t wb = (int64_t)(q_off[b + 1] - q_off[b]) * (kv_end[b] - kv_begin[b]);
     return wa > wb;
   });
+  const int block_m = q_dtype == WF_F32 ? wf::kBlockMF32 : use_dma ? wf::kBlockMDma : wf::kBlockMStaged;
   int64_t items = 0;
   int nc = 0;
   for (int i : order) {
     wf::ChunkDesc& d = p.chunk[nc++];
     d.q_begin = q_off[i];
     d.q_len = q_off[i + 1] - q_off[i];
-    d.ntiles = (d.q_len + wf::kBlockM - 1) / wf::kBlockM;
+    d.ntiles = (d.q_len + block_m - 1) / block_m;
     d.item0 = (int32_t)items;
     d.lead = (int32_t)(kv_begin[i] % 8);
     d.nkeys = (int32_t)(kv_end[i] - kv_begin[i]);
@@ -319,8 +324,10 @@ wf_status wf_chunk_attn_fwd(const wf_kv_cache* c, const void* q, int32_t q_dtype
   hipError_t e;
   if (q_dtype == WF_F32)
     e = wf::launch_attn_f32(p, c->head_dim, (hipStream_t)stream);
+  else if (use_dma)
+    e = wf::launch_attn_bf16_dma(p, c->head_dim, (hipStream_t)stream);
   else if (kvd == WF_BF16)
-    e = wf::launch_attn_bf16(p, c->head_dim, (hipStream_t)stream);
+    e = wf::launch_attn_bf16_staged(p, c->head_dim, (hipStream_t)stream);
   else
     e = wf::launch_attn_fp8kv(p, c->head_dim, (hipStream_t)stream);
   if (e != hipSuccess) return fail(WF_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));

@@ -29,6 +29,8 @@
 // head are 4 * head_dim (2 for Q K^T, 2 for P V).
 #include <type_traits>
 
+#include <type_traits>
+
 #include "wf_internal.h"
 
 namespace wf {
@@ -41,9 +43,10 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int BM = kBlockM;   // query rows per workgroup
-constexpr int BN = 64;        // keys per LDS tile
-constexpr int NT = 256;       // threads per workgroup
+constexpr int BN = 64;             // keys per LDS tile
+constexpr int BM = kBlockMF32;     // query rows per workgroup (fp32 and staged kernels)
+constexpr int NT = 256;            // threads per workgroup (fp32 and staged kernels)
+static_assert(kBlockMF32 == kBlockMStaged, "fp32 and staged kernels share BM");
 constexpr float kLn2 = 0.69314718055994530942f;
 
 __device__ __forceinline__ void locate(const PageMap& m, const FastDiv& divP, const FastDiv& divT,
@@ -85,8 +88,39 @@ __device__ __forceinline__ Item decode_item(const AttnParams& p, int item) {
   return it;
 }
 
+constexpr float kRescaleThreshold = 8.0f;  // log2 units: p <= 2^8 between rescales
+
+// Exact lazy rescaling: the reference point m moves only when a row maximum
+// exceeds it by more than the threshold; O and l are always relative to m.
+template <int D>
+__device__ __forceinline__ void maybe_rescale(float mx, float& m, float& l, f32x16 (&o)[D / 32]) {
+  if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleThreshold) != 0) {
+    const float m_new = fmaxf(m, mx);
+    const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+    m = m_new;
+    l *= alpha;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+  }
+}
+
+// Keep bf16 element e of v only where bit e of m is set.
+__device__ __forceinline__ uint4 mask_bf16x8(uint4 v, uint32_t m) {
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    if (!((m >> e) & 1u)) w[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+namespace staged {
+
 // ---------------------------------------------------------------------------
-// bf16 Q (and bf16 or E4M3FN K/V) kernel.
+// bf16 Q with bf16 or E4M3FN K/V: register-staged tile loads.  Serves E4M3FN
+// caches (converted to bf16 on the way into LDS) and bf16 caches the DMA
+// kernel below does not take (pages under 64 tokens, caches of 4 GiB or more).
 //
 // LDS holds two K tiles and two V^T tiles (bf16).  Rows are padded by 16
 // bytes (K: 64 keys x (2D+16) B; V^T: D dims x (128+16) B) so that the 8 (or
@@ -304,7 +338,6 @@ __device__ __forceinline__ void qk_tile(f32x16 (&s)[2], const char* kbuf, const 
   }
 }
 
-constexpr float kRescaleThreshold = 8.0f;  // log2 units: p <= 2^8 between rescales
 
 template <int D>
 __device__ __forceinline__ void softmax_tile(f32x16 (&s)[2], bf16x8 (&pf)[2][2], f32x16 (&o)[D / 32], float& m,
@@ -477,6 +510,410 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(const AttnParams p
   }
 }
 
+}  // namespace staged
+
+// ---------------------------------------------------------------------------
+// bf16 kernel with LDS-DMA tile loads (bf16 cache, pages >= 64 tokens,
+// cache < 4 GiB).
+//
+// One workgroup = 8 waves (2 per SIMD) = 256 query rows of one head of one
+// chunk; each wave owns 32 rows and keeps its Q^T fragments in VGPRs.  The 8
+// waves share every K/V tile.
+//
+// Tiles reach LDS through global_load_lds_dwordx4 (16 bytes per lane, written
+// to LDS at base + 16 * lane), so no VGPRs stage them.  Layouts (unpadded,
+// 16-byte chunks XOR-swizzled by the low 3 bits of the LDS row):
+//   K half-tile [32 rows][D] bf16: LDS row r holds key pi(r) of the half-tile,
+//     pi(8 j + 4 h + i) = 16 h + 4 j + i.  The MFMA A operand of lane l is
+//     LDS row l % 32, so in the S^T accumulator lane-half h holds the 16
+//     consecutive keys 16 h .. 16 h + 15 of the half-tile.
+//   V^T tile [D][64 keys] bf16, keys in natural order.  Because of pi the 8
+//     keys one P^T operand slot group needs are contiguous: one 16-byte LDS
+//     read per MFMA, and V^T rows are plain 16-byte DMA chunks.
+//
+// Pipeline.  The key range is walked in 32-key half-steps q; one barrier per
+// 64-key tile j (half-steps 2j, 2j+1).  Entering half-step q the wave holds
+// S[q] (masked) and a reference maximum m within 2^8 of S[q]'s row maxima,
+// with O and l relative to m:
+//   [A] S[q+1] = K[q+1] Q^T (MFMA)  ||  P[q] = exp2(S[q] - m), row sums
+//   [B] O^T += V^T[q] P^T[q] (MFMA) ||  mask S[q+1], row max of S[q+1]
+//   [C] rare exact rescale when a row max of S[q+1] exceeds m by more than 8
+// At the start of tile j the DMA for K half-tiles 2j+3, 2j+4 (ring of four)
+// and V tile j+1 (double buffer) is issued into buffers the previous tile
+// freed; V tile j's keys outside the chunk's range are zeroed first if it is
+// an edge tile (0 * NaN would poison P V); the tile ends with a wait for its
+// DMA and a barrier.
+// ---------------------------------------------------------------------------
+namespace dma {
+
+constexpr int NW = 8;         // waves per workgroup
+constexpr int NTD = 64 * NW;  // threads per workgroup
+constexpr int BMD = 32 * NW;  // query rows per workgroup
+constexpr int HK = 32;        // keys per K half-tile
+static_assert(BMD == kBlockMDma, "host and kernel disagree on the DMA kernel block size");
+
+template <int D>
+struct Geo {
+  static constexpr int KROWB = 2 * D;              // bytes per K row
+  static constexpr int KHALF = HK * KROWB;         // bytes per K half-tile
+  static constexpr int VTILE = D * 2 * BN;         // V^T: D rows of 128 bytes
+  static constexpr int KDMA = KHALF / 1024;        // DMA instructions per K half-tile
+  static constexpr int VDMA = VTILE / 1024 / NW;   // DMA instructions per wave per V tile
+  static_assert(KDMA <= NW && VDMA >= 1, "tile shapes do not match the wave count");
+};
+
+// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt[3:0] | vmcnt[5:4] << 14,
+// expcnt[6:4] = 7, lgkmcnt[11:8] = 15).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt out of range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+__device__ __forceinline__ void dma16(const void* src, void* lds) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                   (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+
+// Uniform geometry of the key run starting at tile-relative key `rel0`:
+// byte offsets relative to the cache base pointers including the run's
+// first-key offset; kb1/vb1 are biased by -P so that the same per-key formula
+// holds past the page break.  Keys [0, split) of the run are in the first page.
+struct RunGeom {
+  uint32_t kb0, kb1, vb0, vb1;
+  int32_t split;
+};
+
+template <int D>
+__device__ __forceinline__ RunGeom run_geom(const AttnParams& p, const ChunkDesc& cd, int head, int rel0) {
+  const uint32_t x = (uint32_t)cd.map.base_off + (uint32_t)rel0;
+  const uint32_t pg = fastdiv(x, p.divP);
+  const int32_t off0 = (int32_t)(x - pg * p.divP.d);
+  uint32_t slot = (uint32_t)cd.map.base_slot + pg;
+  slot -= fastdiv(slot, p.divT) * p.divT.d;
+  const uint32_t slot1 = slot + 1 == (uint32_t)p.T ? 0u : slot + 1;
+  const int64_t r0 = (int64_t)p.table[slot] * p.H + head, r1 = (int64_t)p.table[slot1] * p.H + head;
+  RunGeom g;
+  g.split = p.P - off0;
+  g.kb0 = (uint32_t)((r0 * p.P + off0) * (2 * D));
+  g.kb1 = (uint32_t)((r1 * p.P + off0 - p.P) * (2 * D));
+  g.vb0 = (uint32_t)((r0 * D * p.P + off0) * 2);
+  g.vb1 = (uint32_t)((r1 * D * p.P + off0 - p.P) * 2);
+  return g;
+}
+
+// Per-lane constants of this wave's DMA instructions: source byte offset
+// relative to the run geometry base and the run-relative key of the 16-byte
+// chunk (for the page-break select).  Wave w issues K instruction w of a half
+// tile (if w < KDMA) and V instructions w * VDMA + r of a tile.
+template <int D>
+struct DmaPlan {
+  uint32_t koff;
+  int32_t kkey;
+  uint32_t voff[Geo<D>::VDMA];
+  int32_t vkey[Geo<D>::VDMA];
+};
+
+template <int D>
+__device__ __forceinline__ DmaPlan<D> make_plan(int wave, int lane, int P) {
+  using G = Geo<D>;
+  DmaPlan<D> pl;
+  {
+    const int y = 1024 * wave + 16 * lane;  // LDS byte inside the K half-tile
+    const int row = y / G::KROWB, pc = (y % G::KROWB) / 16;
+    const int lc = pc ^ (row & 7);
+    const int key = 16 * ((row >> 2) & 1) + 4 * (row >> 3) + (row & 3);  // pi(row)
+    pl.kkey = key;
+    pl.koff = (uint32_t)(key * G::KROWB + lc * 16);
+  }
+#pragma unroll
+  for (int r = 0; r < G::VDMA; ++r) {
+    const int y = 1024 * (wave * G::VDMA + r) + 16 * lane;  // LDS byte inside the V^T tile
+    const int d = y / 128, pc = (y % 128) / 16;
+    const int lc = pc ^ (d & 7);
+    pl.vkey[r] = lc * 8;
+    pl.voff[r] = (uint32_t)(d * P * 2 + lc * 16);
+  }
+  return pl;
+}
+
+// DMA K half-tile q (keys 32 q .. 32 q + 31 of the chunk's tile grid).
+template <int D>
+__device__ __forceinline__ void dma_k(const AttnParams& p, const ChunkDesc& cd, int head, int q,
+                                      const DmaPlan<D>& pl, char* khalf, int wave) {
+  using G = Geo<D>;
+  if (G::KDMA < NW && wave >= G::KDMA) return;
+  const RunGeom g = run_geom<D>(p, cd, head, q * HK);
+  const uint32_t off = (pl.kkey < g.split ? g.kb0 : g.kb1) + pl.koff;
+  dma16((const char*)p.k + off, khalf + 1024 * wave);
+}
+
+// DMA V^T tile t (keys 64 t .. 64 t + 63).
+template <int D>
+__device__ __forceinline__ void dma_v(const AttnParams& p, const ChunkDesc& cd, int head, int t,
+                                      const DmaPlan<D>& pl, char* vbuf, int wave) {
+  using G = Geo<D>;
+  const RunGeom g = run_geom<D>(p, cd, head, t * BN);
+#pragma unroll
+  for (int r = 0; r < G::VDMA; ++r) {
+    const uint32_t off = (pl.vkey[r] < g.split ? g.vb0 : g.vb1) + pl.voff[r];
+    dma16((const char*)p.v + off, vbuf + 1024 * (wave * G::VDMA + r));
+  }
+}
+
+// Zero the keys of V^T tile t (in LDS) that lie outside [lo, hi).
+template <int D>
+__device__ __forceinline__ void zero_v_outside(char* vbuf, int t, int lo, int hi) {
+  for (int idx = threadIdx.x; idx < D * 8; idx += NTD) {
+    const int d = idx >> 3, c = idx & 7;
+    const int rel = t * BN + 8 * c;
+    if (rel >= lo && rel + 8 <= hi) continue;
+    uint32_t m = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) m |= (rel + e >= lo && rel + e < hi) ? 1u << e : 0u;
+    uint4* a = (uint4*)(vbuf + d * 128 + 16 * (c ^ (d & 7)));
+    *a = mask_bf16x8(*a, m);
+  }
+}
+
+// One 32-key half-step as explicitly ordered stages.  Stage i of [A] issues
+// the LDS read of the K fragment two stages ahead, one MFMA of the S[q+1]
+// chain (k-step i), and exponent / bf16 packing / row sum for two elements of
+// S[q].  Stage i of [B] issues the V fragment read two stages ahead, one O^T
+// MFMA (d block i % DB, P slot group i / DB), and masking + row max for two
+// elements of S[q+1].  Stages are separated by scheduling barriers and each
+// stage's VALU results are pinned with empty asm statements, so at most three
+// fragments are live and every MFMA is followed by independent VALU work.
+// kx[t] / vx[u] are per-lane LDS byte offsets of the swizzled chunks.
+template <int D, bool MASK>
+__device__ __forceinline__ float half_step(const f32x16& s_cur, f32x16& s_next, f32x16 (&o)[D / 32],
+                                           const bf16x8 (&qf)[D / 16], const char* khalf, const char* vtile,
+                                           const int (&kx)[4], int vx0, int vx1, float m, float& l,
+                                           float sl2, int key_next0, int lo, int hi, int hf) {
+  constexpr int NA = D / 16;        // QK^T MFMAs (k-steps) per half-step
+  constexpr int NB = 2 * (D / 32);  // PV MFMAs per half-step
+  constexpr int DB = D / 32;
+  constexpr int EA = 16 / NA;       // S[q] elements per [A] stage
+  constexpr int EB = 16 / NB;       // S[q+1] elements per [B] stage
+  typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+  const bf16x2v ones = {(__bf16)1.0f, (__bf16)1.0f};
+  const float nm = -m;
+  bf16x8 pf[2];
+  bf16x8 frag[3];
+  float lsum[2] = {0.f, 0.f};
+  auto kaddr = [&](int ks) { return (const bf16x8*)(khalf + kx[ks & 3] + (ks >> 2) * 128); };
+  frag[0] = *kaddr(0);
+  frag[1] = *kaddr(1);
+#pragma unroll
+  for (int i = 0; i < NA; ++i) {
+    if (i + 2 < NA) frag[(i + 2) % 3] = *kaddr(i + 2);
+    if (i == 0) {
+      f32x16 z;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) z[e] = 0.f;
+      s_next = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag[0], qf[0], z, 0, 0, 0);
+    } else {
+      s_next = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag[i % 3], qf[i], s_next, 0, 0, 0);
+    }
+#pragma unroll
+    for (int e = EA * i; e < EA * (i + 1); e += 2) {
+      const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[e], sl2, nm));
+      const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[e + 1], sl2, nm));
+      const bf16x2v pk = {(__bf16)e0, (__bf16)e1};
+      pf[e >> 3][e & 7] = pk[0];
+      pf[e >> 3][(e & 7) + 1] = pk[1];
+      lsum[(e >> 1) & 1] = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, lsum[(e >> 1) & 1], false);
+    }
+    asm volatile("" : "+v"(lsum[0]), "+v"(lsum[1]));
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  l += lsum[0] + lsum[1];
+  auto vaddr = [&](int i) { return (const bf16x8*)(vtile + (i / DB ? vx1 : vx0) + (i % DB) * 32 * 128); };
+  frag[0] = *vaddr(0);
+  frag[1] = *vaddr(1);
+  float mx[2] = {-INFINITY, -INFINITY};
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    if (i + 2 < NB) frag[(i + 2) % 3] = *vaddr(i + 2);
+    o[i % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag[i % 3], pf[i / DB], o[i % DB], 0, 0, 0);
+#pragma unroll
+    for (int e = EB * i; e < EB * (i + 1); e += 2) {
+      float a0 = s_next[e], a1 = s_next[e + 1];
+      if constexpr (MASK) {
+        const int key = key_next0 + 16 * hf + e;  // key of S^T element e
+        a0 = (key >= lo && key < hi) ? a0 : -INFINITY;
+        a1 = (key + 1 >= lo && key + 1 < hi) ? a1 : -INFINITY;
+        s_next[e] = a0;
+        s_next[e + 1] = a1;
+      }
+      mx[(e >> 1) & 1] = fmaxf(mx[(e >> 1) & 1], fmaxf(a0, a1));
+    }
+    asm volatile("" : "+v"(mx[0]), "+v"(mx[1]));
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  return half_max(fmaxf(mx[0], mx[1])) * sl2;
+}
+
+template <int D>
+__global__ __launch_bounds__(NTD, 2) void attn_fwd_dma_kernel(const AttnParams p) {
+  using G = Geo<D>;
+  constexpr int KS = D / 16;
+  constexpr int DB = D / 32;
+  // K half-tiles in a ring of four; V^T tiles double-buffered.  Separate LDS
+  // objects let the compiler see that DMA into one buffer does not alias
+  // reads of another.
+  __shared__ __align__(1024) char kh0[G::KHALF];
+  __shared__ __align__(1024) char kh1[G::KHALF];
+  __shared__ __align__(1024) char kh2[G::KHALF];
+  __shared__ __align__(1024) char kh3[G::KHALF];
+  __shared__ __align__(1024) char vbuf0[G::VTILE];
+  __shared__ __align__(1024) char vbuf1[G::VTILE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int lq = lane & 31;  // query column owned by this lane
+  const int hf = lane >> 5;  // 32-lane half
+  const int sw = lq & 7;     // swizzle of this lane's LDS rows
+
+  const Item it = decode_item(p, blockIdx.x);
+  const ChunkDesc cd = p.chunk[it.c];
+  const int head = it.head;
+  const int qrow = it.qt * BMD + wave * 32 + lq;
+  const int row = cd.q_begin + qrow;
+  const bool row_ok = qrow < cd.q_len;
+  const int lo = cd.lead, hi = cd.lead + cd.nkeys;
+  const int nt = (hi + BN - 1) / BN;  // 64-key tiles
+  const int nh = (hi + HK - 1) / HK;  // 32-key half-tiles
+  const float sl2 = p.scale_log2;
+  const DmaPlan<D> plan = make_plan<D>(wave, lane, p.P);
+
+  int kx[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) kx[t] = lq * G::KROWB + 16 * ((2 * t + hf) ^ sw);
+  // V^T chunk offsets: half h of a tile, slot group u -> keys 32 h + 16 hf + 8 u
+  int vx[2][2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) vx[h][u] = lq * 128 + 16 * ((4 * h + 2 * hf + u) ^ sw);
+
+  // K half-tiles 0..2 and V tile 0 in flight while Q is fetched
+  dma_k<D>(p, cd, head, 0, plan, kh0, wave);
+  if (nh > 1) dma_k<D>(p, cd, head, 1, plan, kh1, wave);
+  if (nh > 2) dma_k<D>(p, cd, head, 2, plan, kh2, wave);
+  dma_v<D>(p, cd, head, 0, plan, vbuf0, wave);
+
+  bf16x8 qf[KS];
+  {
+    const __bf16* qp = (const __bf16*)p.q + ((int64_t)row * p.H + head) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (row_ok) v = *(const uint4*)(qp + ks * 16 + hf * 8);
+      qf[ks] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+  f32x16 o[DB];
+#pragma unroll
+  for (int b = 0; b < DB; ++b)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[b][i] = 0.f;
+  float l = 0.f;
+
+  auto edge = [&](int t) { return t * BN < lo || t * BN + BN > hi; };    // 64-key tile t
+  auto hedge = [&](int q) { return q * HK < lo || q * HK + HK > hi; };  // 32-key half-tile q
+
+  wait_vmcnt<0>();
+  __syncthreads();
+  if (edge(0)) {
+    zero_v_outside<D>(vbuf0, 0, lo, hi);
+    __syncthreads();
+  }
+  // S of half-tile 0 (it holds key lo < 8, so its row maxima are finite)
+  f32x16 sa, sb;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) sa[i] = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const bf16x8 kf = *(const bf16x8*)(kh0 + kx[ks & 3] + (ks >> 2) * 128);
+    sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sa, 0, 0, 0);
+  }
+  float m;
+  {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int key = 16 * hf + i;
+      sa[i] = (key >= lo && key < hi) ? sa[i] : -INFINITY;
+      mx = fmaxf(mx, sa[i]);
+    }
+    m = half_max(mx) * sl2;
+  }
+  __syncthreads();  // kh0 is free for half-tile 4
+
+  // Tile step j: half-steps 2j (S in sa) and 2j+1 (S in sb).  EVEN selects
+  // the ring parity: even j reads K halves in kh1, kh2 and refills kh3, kh0;
+  // odd j reads kh3, kh0 and refills kh1, kh2.  M0 / M1: half-tiles 2j+1 /
+  // 2j+2 need masking.
+  auto step = [&](auto even_tag, auto m0_tag, auto m1_tag, int j) {
+    constexpr bool even = decltype(even_tag)::value;
+    char* const k_a = even ? kh1 : kh3;   // half-tile 2j+1
+    char* const k_b = even ? kh2 : kh0;   // half-tile 2j+2
+    char* const k_f0 = even ? kh3 : kh1;  // receives half-tile 2j+3
+    char* const k_f1 = even ? kh0 : kh2;  // receives half-tile 2j+4
+    char* const vb_cur = even ? vbuf0 : vbuf1;
+    char* const vb_free = even ? vbuf1 : vbuf0;
+    if (2 * j + 3 < nh) dma_k<D>(p, cd, head, 2 * j + 3, plan, k_f0, wave);
+    if (2 * j + 4 < nh) dma_k<D>(p, cd, head, 2 * j + 4, plan, k_f1, wave);
+    if (j + 1 < nt) dma_v<D>(p, cd, head, j + 1, plan, vb_free, wave);
+    if (j > 0 && edge(j)) {
+      zero_v_outside<D>(vb_cur, j, lo, hi);
+      __syncthreads();
+    }
+    float mx = half_step<D, decltype(m0_tag)::value>(sa, sb, o, qf, k_a, vb_cur, kx, vx[0][0], vx[0][1], m, l,
+                                                     sl2, (2 * j + 1) * HK, lo, hi, hf);
+    if (2 * j + 1 < nh) {
+      maybe_rescale<D>(mx, m, l, o);
+      mx = half_step<D, decltype(m1_tag)::value>(sb, sa, o, qf, k_b, vb_cur, kx, vx[1][0], vx[1][1], m, l,
+                                                 sl2, (2 * j + 2) * HK, lo, hi, hf);
+      if (2 * j + 2 < nh) maybe_rescale<D>(mx, m, l, o);
+    }
+    wait_vmcnt<0>();
+    __syncthreads();
+  };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  auto dispatch = [&](auto even_tag, int j) {
+    const bool e1 = hedge(2 * j + 1), e2 = hedge(2 * j + 2);
+    if (!e1 && !e2)
+      step(even_tag, F_{}, F_{}, j);
+    else
+      step(even_tag, T_{}, T_{}, j);
+  };
+  for (int j = 0; j < nt; j += 2) {
+    dispatch(T_{}, j);
+    if (j + 1 < nt) dispatch(F_{}, j + 1);
+  }
+
+  const float lt = half_sum(l);
+  const float inv = 1.f / lt;
+  if (row_ok) {
+    __bf16* orow = (__bf16*)p.o + ((int64_t)row * p.H + head) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 v = {(__bf16)(o[db][4 * g + 0] * inv), (__bf16)(o[db][4 * g + 1] * inv),
+                    (__bf16)(o[db][4 * g + 2] * inv), (__bf16)(o[db][4 * g + 3] * inv)};
+        *(bf16x4*)(orow + db * 32 + 8 * g + 4 * hf) = v;
+      }
+    if (p.lse != nullptr && hf == 0) p.lse[(int64_t)head * p.nq + row] = (m + __log2f(lt)) * kLn2;
+  }
+}
+
+}  // namespace dma
+
 // ---------------------------------------------------------------------------
 // fp32 kernel (tight-tolerance path): V_MFMA_F32_32X32X2_F32, 32-key tiles,
 // single-buffered.  Same S^T formulation as the bf16 kernel.
@@ -602,25 +1039,34 @@ __global__ __launch_bounds__(NT) void attn_fwd_f32_kernel(const AttnParams p) {
   }
 }
 
+
 template <int D, bool FP8KV>
-hipError_t launch_bf16_t(const AttnParams& p, hipStream_t s) {
-  const size_t lds = Geo<D, FP8KV>::LDS;
+hipError_t launch_staged_t(const AttnParams& p, hipStream_t s) {
+  const size_t lds = staged::Geo<D, FP8KV>::LDS;
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&attn_fwd_bf16_kernel<D, FP8KV>),
+      reinterpret_cast<const void*>(&staged::attn_fwd_bf16_kernel<D, FP8KV>),
       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, FP8KV>), dim3(p.num_items), dim3(NT), lds, s, p);
+  hipLaunchKernelGGL((staged::attn_fwd_bf16_kernel<D, FP8KV>), dim3(p.num_items), dim3(NT), lds, s, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_attn_bf16(const AttnParams& p, int head_dim, hipStream_t s) {
-  return head_dim == 128 ? launch_bf16_t<128, false>(p, s) : launch_bf16_t<64, false>(p, s);
+hipError_t launch_attn_bf16_dma(const AttnParams& p, int head_dim, hipStream_t s) {
+  if (head_dim == 128)
+    hipLaunchKernelGGL(dma::attn_fwd_dma_kernel<128>, dim3(p.num_items), dim3(dma::NTD), 0, s, p);
+  else
+    hipLaunchKernelGGL(dma::attn_fwd_dma_kernel<64>, dim3(p.num_items), dim3(dma::NTD), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_bf16_staged(const AttnParams& p, int head_dim, hipStream_t s) {
+  return head_dim == 128 ? launch_staged_t<128, false>(p, s) : launch_staged_t<64, false>(p, s);
 }
 
 hipError_t launch_attn_fp8kv(const AttnParams& p, int head_dim, hipStream_t s) {
-  return head_dim == 128 ? launch_bf16_t<128, true>(p, s) : launch_bf16_t<64, true>(p, s);
+  return head_dim == 128 ? launch_staged_t<128, true>(p, s) : launch_staged_t<64, true>(p, s);
 }
 
 hipError_t launch_attn_f32(const AttnParams& p, int head_dim, hipStream_t s) {

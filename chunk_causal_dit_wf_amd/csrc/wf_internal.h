@@ -107,10 +107,13 @@ struct AttnParams {
   int32_t table[WF_MAX_TABLE_LEN];
 };
 
-// Query rows per workgroup of each instantiation (host needs it for the grid).
-constexpr int kBlockM = 128;
+// Query rows per workgroup of each attention kernel (the host needs them for the grid).
+constexpr int kBlockMF32 = 128;     // fp32 kernel
+constexpr int kBlockMStaged = 128;  // bf16 Q, register-staged tile loads (E4M3FN or small pages)
+constexpr int kBlockMDma = 256;     // bf16 Q and cache, LDS-DMA tile loads
 
-hipError_t launch_attn_bf16(const AttnParams& p, int head_dim, hipStream_t s);
+hipError_t launch_attn_bf16_dma(const AttnParams& p, int head_dim, hipStream_t s);
+hipError_t launch_attn_bf16_staged(const AttnParams& p, int head_dim, hipStream_t s);
 hipError_t launch_attn_f32(const AttnParams& p, int head_dim, hipStream_t s);
 hipError_t launch_attn_fp8kv(const AttnParams& p, int head_dim, hipStream_t s);
 
