@@ -521,8 +521,10 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(const AttnParams p
 // waves share every K/V tile.
 //
 // Tiles reach LDS through global_load_lds_dwordx4 (16 bytes per lane, written
-// to LDS at base + 16 * lane), so no VGPRs stage them.  Layouts (unpadded,
-// 16-byte chunks XOR-swizzled by the low 3 bits of the LDS row):
+// to LDS at base + 16 * lane), so no VGPRs stage them.  Rows are padded by 16
+// bytes (K: 2D+16 bytes, V^T: 144 bytes) so that the 16 lanes one LDS cycle
+// serves hit distinct banks and every fragment read is an immediate offset
+// from one per-lane base; DMA lanes that land on padding load a dummy chunk.
 //   K half-tile [32 rows][D] bf16: LDS row r holds key pi(r) of the half-tile,
 //     pi(8 j + 4 h + i) = 16 h + 4 j + i.  The MFMA A operand of lane l is
 //     LDS row l % 32, so in the S^T accumulator lane-half h holds the 16
@@ -554,12 +556,15 @@ static_assert(BMD == kBlockMDma, "host and kernel disagree on the DMA kernel blo
 
 template <int D>
 struct Geo {
-  static constexpr int KROWB = 2 * D;              // bytes per K row
-  static constexpr int KHALF = HK * KROWB;         // bytes per K half-tile
-  static constexpr int VTILE = D * 2 * BN;         // V^T: D rows of 128 bytes
-  static constexpr int KDMA = KHALF / 1024;        // DMA instructions per K half-tile
-  static constexpr int VDMA = VTILE / 1024 / NW;   // DMA instructions per wave per V tile
-  static_assert(KDMA <= NW && VDMA >= 1, "tile shapes do not match the wave count");
+  static constexpr int KROW = 2 * D + 16;                 // LDS bytes per K row (padded)
+  static constexpr int KCH = D / 8;                       // 16-byte data chunks per K row
+  static constexpr int KDMA = (HK * KROW + 1023) / 1024;  // DMA instructions per K half-tile
+  static constexpr int KHALF = KDMA * 1024;               // LDS bytes per K half-tile buffer
+  static constexpr int VROW = 2 * BN + 16;                // LDS bytes per V^T row (padded)
+  static constexpr int VDMA = (D * VROW + 1023) / 1024;   // DMA instructions per V^T tile
+  static constexpr int VTILE = VDMA * 1024;               // LDS bytes per V^T tile buffer
+  static constexpr int KPW = (KDMA + NW - 1) / NW;        // max K instructions per wave
+  static constexpr int VPW = (VDMA + NW - 1) / NW;        // max V instructions per wave
 };
 
 // s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt[3:0] | vmcnt[5:4] << 14,
@@ -575,89 +580,116 @@ __device__ __forceinline__ void dma16(const void* src, void* lds) {
                                    (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
 }
 
-// Uniform geometry of the key run starting at tile-relative key `rel0`:
-// byte offsets relative to the cache base pointers including the run's
-// first-key offset; kb1/vb1 are biased by -P so that the same per-key formula
-// holds past the page break.  Keys [0, split) of the run are in the first page.
+// Scalar cursor over the chunk's keys for one DMA stream: ring slot and
+// in-page offset of the next run to load.  A run (32 or 64 keys) spans at
+// most two pages (pages hold >= 64 keys).  For key k of the run (0-based),
+// the K row is at byte (k < split ? kb0 : kb1) + k * 2D and the V^T column at
+// (k < split ? vb0 : vb1) + d * P * 2 + k * 2, relative to the cache bases;
+// kb1 / vb1 are biased by -P so one formula serves both pages.
+struct Cursor {
+  int32_t slot, off;
+};
 struct RunGeom {
   uint32_t kb0, kb1, vb0, vb1;
   int32_t split;
 };
 
-template <int D>
-__device__ __forceinline__ RunGeom run_geom(const AttnParams& p, const ChunkDesc& cd, int head, int rel0) {
+__device__ __forceinline__ Cursor cursor_at(const AttnParams& p, const ChunkDesc& cd, int rel0) {
   const uint32_t x = (uint32_t)cd.map.base_off + (uint32_t)rel0;
   const uint32_t pg = fastdiv(x, p.divP);
-  const int32_t off0 = (int32_t)(x - pg * p.divP.d);
+  Cursor c;
+  c.off = (int32_t)(x - pg * p.divP.d);
   uint32_t slot = (uint32_t)cd.map.base_slot + pg;
-  slot -= fastdiv(slot, p.divT) * p.divT.d;
-  const uint32_t slot1 = slot + 1 == (uint32_t)p.T ? 0u : slot + 1;
-  const int64_t r0 = (int64_t)p.table[slot] * p.H + head, r1 = (int64_t)p.table[slot1] * p.H + head;
+  c.slot = (int32_t)(slot - fastdiv(slot, p.divT) * p.divT.d);
+  return c;
+}
+
+template <int D>
+__device__ __forceinline__ RunGeom run_geom(const AttnParams& p, int head, const Cursor& c) {
+  const int slot1 = c.slot + 1 == p.T ? 0 : c.slot + 1;
+  const uint32_t b0 = (uint32_t)(p.table[c.slot] * p.H + head), b1 = (uint32_t)(p.table[slot1] * p.H + head);
+  const uint32_t P = (uint32_t)p.P;
   RunGeom g;
-  g.split = p.P - off0;
-  g.kb0 = (uint32_t)((r0 * p.P + off0) * (2 * D));
-  g.kb1 = (uint32_t)((r1 * p.P + off0 - p.P) * (2 * D));
-  g.vb0 = (uint32_t)((r0 * D * p.P + off0) * 2);
-  g.vb1 = (uint32_t)((r1 * D * p.P + off0 - p.P) * 2);
+  g.split = p.P - c.off;
+  g.kb0 = (b0 * P + (uint32_t)c.off) * (2 * D);
+  g.kb1 = (b1 * P + (uint32_t)c.off - P) * (2 * D);
+  g.vb0 = (b0 * (uint32_t)D * P + (uint32_t)c.off) * 2;
+  g.vb1 = (b1 * (uint32_t)D * P + (uint32_t)c.off - P) * 2;
   return g;
+}
+
+__device__ __forceinline__ void advance(const AttnParams& p, Cursor& c, int n) {
+  c.off += n;
+  if (c.off >= p.P) {
+    c.off -= p.P;
+    c.slot = c.slot + 1 == p.T ? 0 : c.slot + 1;
+  }
 }
 
 // Per-lane constants of this wave's DMA instructions: source byte offset
 // relative to the run geometry base and the run-relative key of the 16-byte
-// chunk (for the page-break select).  Wave w issues K instruction w of a half
-// tile (if w < KDMA) and V instructions w * VDMA + r of a tile.
+// chunk (for the page-break select).  Wave w issues instructions w, w + NW, ...
+// of each K half-tile and V^T tile.  Lanes that land on row padding (or past
+// the last row) load the run's first chunk, a valid address, into the slack.
 template <int D>
 struct DmaPlan {
-  uint32_t koff;
-  int32_t kkey;
-  uint32_t voff[Geo<D>::VDMA];
-  int32_t vkey[Geo<D>::VDMA];
+  uint32_t koff[Geo<D>::KPW];
+  int32_t kkey[Geo<D>::KPW];
+  uint32_t voff[Geo<D>::VPW];
+  int32_t vkey[Geo<D>::VPW];
 };
 
 template <int D>
 __device__ __forceinline__ DmaPlan<D> make_plan(int wave, int lane, int P) {
   using G = Geo<D>;
   DmaPlan<D> pl;
-  {
-    const int y = 1024 * wave + 16 * lane;  // LDS byte inside the K half-tile
-    const int row = y / G::KROWB, pc = (y % G::KROWB) / 16;
-    const int lc = pc ^ (row & 7);
+#pragma unroll
+  for (int r = 0; r < G::KPW; ++r) {
+    const int y = 1024 * (wave + NW * r) + 16 * lane;  // LDS byte inside the K half-tile buffer
+    const int row = y / G::KROW, pc = (y % G::KROW) / 16;
+    const bool data = row < HK && pc < G::KCH;
     const int key = 16 * ((row >> 2) & 1) + 4 * (row >> 3) + (row & 3);  // pi(row)
-    pl.kkey = key;
-    pl.koff = (uint32_t)(key * G::KROWB + lc * 16);
+    pl.kkey[r] = data ? key : 0;
+    pl.koff[r] = data ? (uint32_t)(key * 2 * D + pc * 16) : 0u;
   }
 #pragma unroll
-  for (int r = 0; r < G::VDMA; ++r) {
-    const int y = 1024 * (wave * G::VDMA + r) + 16 * lane;  // LDS byte inside the V^T tile
-    const int d = y / 128, pc = (y % 128) / 16;
-    const int lc = pc ^ (d & 7);
-    pl.vkey[r] = lc * 8;
-    pl.voff[r] = (uint32_t)(d * P * 2 + lc * 16);
+  for (int r = 0; r < G::VPW; ++r) {
+    const int y = 1024 * (wave + NW * r) + 16 * lane;  // LDS byte inside the V^T tile buffer
+    const int d = y / G::VROW, pc = (y % G::VROW) / 16;
+    const bool data = d < D && pc < 8;
+    pl.vkey[r] = data ? pc * 8 : 0;
+    pl.voff[r] = data ? (uint32_t)(d * P * 2 + pc * 16) : 0u;
   }
   return pl;
 }
 
-// DMA K half-tile q (keys 32 q .. 32 q + 31 of the chunk's tile grid).
+// DMA the K half-tile at cursor c (32 keys) into khalf.
 template <int D>
-__device__ __forceinline__ void dma_k(const AttnParams& p, const ChunkDesc& cd, int head, int q,
-                                      const DmaPlan<D>& pl, char* khalf, int wave) {
+__device__ __forceinline__ void dma_k(const AttnParams& p, int head, const Cursor& c, const DmaPlan<D>& pl,
+                                      char* khalf, int wave) {
   using G = Geo<D>;
-  if (G::KDMA < NW && wave >= G::KDMA) return;
-  const RunGeom g = run_geom<D>(p, cd, head, q * HK);
-  const uint32_t off = (pl.kkey < g.split ? g.kb0 : g.kb1) + pl.koff;
-  dma16((const char*)p.k + off, khalf + 1024 * wave);
+  const RunGeom g = run_geom<D>(p, head, c);
+#pragma unroll
+  for (int r = 0; r < G::KPW; ++r) {
+    if (wave + NW * r < G::KDMA) {
+      const uint32_t off = (pl.kkey[r] < g.split ? g.kb0 : g.kb1) + pl.koff[r];
+      dma16((const char*)p.k + off, khalf + 1024 * (wave + NW * r));
+    }
+  }
 }
 
-// DMA V^T tile t (keys 64 t .. 64 t + 63).
+// DMA the V^T tile at cursor c (64 keys) into vbuf.
 template <int D>
-__device__ __forceinline__ void dma_v(const AttnParams& p, const ChunkDesc& cd, int head, int t,
-                                      const DmaPlan<D>& pl, char* vbuf, int wave) {
+__device__ __forceinline__ void dma_v(const AttnParams& p, int head, const Cursor& c, const DmaPlan<D>& pl,
+                                      char* vbuf, int wave) {
   using G = Geo<D>;
-  const RunGeom g = run_geom<D>(p, cd, head, t * BN);
+  const RunGeom g = run_geom<D>(p, head, c);
 #pragma unroll
-  for (int r = 0; r < G::VDMA; ++r) {
-    const uint32_t off = (pl.vkey[r] < g.split ? g.vb0 : g.vb1) + pl.voff[r];
-    dma16((const char*)p.v + off, vbuf + 1024 * (wave * G::VDMA + r));
+  for (int r = 0; r < G::VPW; ++r) {
+    if (wave + NW * r < G::VDMA) {
+      const uint32_t off = (pl.vkey[r] < g.split ? g.vb0 : g.vb1) + pl.voff[r];
+      dma16((const char*)p.v + off, vbuf + 1024 * (wave + NW * r));
+    }
   }
 }
 
@@ -671,7 +703,7 @@ __device__ __forceinline__ void zero_v_outside(char* vbuf, int t, int lo, int hi
     uint32_t m = 0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) m |= (rel + e >= lo && rel + e < hi) ? 1u << e : 0u;
-    uint4* a = (uint4*)(vbuf + d * 128 + 16 * (c ^ (d & 7)));
+    uint4* a = (uint4*)(vbuf + d * Geo<D>::VROW + 16 * c);
     *a = mask_bf16x8(*a, m);
   }
 }
@@ -684,11 +716,12 @@ __device__ __forceinline__ void zero_v_outside(char* vbuf, int t, int lo, int hi
 // elements of S[q+1].  Stages are separated by scheduling barriers and each
 // stage's VALU results are pinned with empty asm statements, so at most three
 // fragments are live and every MFMA is followed by independent VALU work.
-// kx[t] / vx[u] are per-lane LDS byte offsets of the swizzled chunks.
+// kx / vx are this lane's LDS byte offsets of its K row chunk (k-step 0) and
+// of its V^T row chunk (d block 0, slot group 0).
 template <int D, bool MASK>
 __device__ __forceinline__ float half_step(const f32x16& s_cur, f32x16& s_next, f32x16 (&o)[D / 32],
                                            const bf16x8 (&qf)[D / 16], const char* khalf, const char* vtile,
-                                           const int (&kx)[4], int vx0, int vx1, float m, float& l,
+                                           int kx, int vx, float m, float& l,
                                            float sl2, int key_next0, int lo, int hi, int hf) {
   constexpr int NA = D / 16;        // QK^T MFMAs (k-steps) per half-step
   constexpr int NB = 2 * (D / 32);  // PV MFMAs per half-step
@@ -701,7 +734,7 @@ __device__ __forceinline__ float half_step(const f32x16& s_cur, f32x16& s_next, 
   bf16x8 pf[2];
   bf16x8 frag[3];
   float lsum[2] = {0.f, 0.f};
-  auto kaddr = [&](int ks) { return (const bf16x8*)(khalf + kx[ks & 3] + (ks >> 2) * 128); };
+  auto kaddr = [&](int ks) { return (const bf16x8*)(khalf + kx + 32 * ks); };
   frag[0] = *kaddr(0);
   frag[1] = *kaddr(1);
 #pragma unroll
@@ -728,7 +761,7 @@ __device__ __forceinline__ float half_step(const f32x16& s_cur, f32x16& s_next, 
     __builtin_amdgcn_sched_barrier(0);
   }
   l += lsum[0] + lsum[1];
-  auto vaddr = [&](int i) { return (const bf16x8*)(vtile + (i / DB ? vx1 : vx0) + (i % DB) * 32 * 128); };
+  auto vaddr = [&](int i) { return (const bf16x8*)(vtile + vx + 16 * (i / DB) + (i % DB) * 32 * Geo<D>::VROW); };
   frag[0] = *vaddr(0);
   frag[1] = *vaddr(1);
   float mx[2] = {-INFINITY, -INFINITY};
@@ -771,10 +804,9 @@ __global__ __launch_bounds__(NTD, 2) void attn_fwd_dma_kernel(const AttnParams p
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lq = lane & 31;  // query column owned by this lane
   const int hf = lane >> 5;  // 32-lane half
-  const int sw = lq & 7;     // swizzle of this lane's LDS rows
 
   const Item it = decode_item(p, blockIdx.x);
   const ChunkDesc cd = p.chunk[it.c];
@@ -787,22 +819,20 @@ __global__ __launch_bounds__(NTD, 2) void attn_fwd_dma_kernel(const AttnParams p
   const int nh = (hi + HK - 1) / HK;  // 32-key half-tiles
   const float sl2 = p.scale_log2;
   const DmaPlan<D> plan = make_plan<D>(wave, lane, p.P);
-
-  int kx[4];
-#pragma unroll
-  for (int t = 0; t < 4; ++t) kx[t] = lq * G::KROWB + 16 * ((2 * t + hf) ^ sw);
-  // V^T chunk offsets: half h of a tile, slot group u -> keys 32 h + 16 hf + 8 u
-  int vx[2][2];
-#pragma unroll
-  for (int h = 0; h < 2; ++h)
-#pragma unroll
-    for (int u = 0; u < 2; ++u) vx[h][u] = lq * 128 + 16 * ((4 * h + 2 * hf + u) ^ sw);
+  const int kx = lq * G::KROW + 16 * hf;          // K row lq, chunk hf (k-step 0)
+  const int vx0 = lq * G::VROW + 16 * (2 * hf);      // V^T row lq, keys 16 hf .. (first half of a tile)
+  const int vx1 = lq * G::VROW + 16 * (4 + 2 * hf);  // ... keys 32 + 16 hf .. (second half)
 
   // K half-tiles 0..2 and V tile 0 in flight while Q is fetched
-  dma_k<D>(p, cd, head, 0, plan, kh0, wave);
-  if (nh > 1) dma_k<D>(p, cd, head, 1, plan, kh1, wave);
-  if (nh > 2) dma_k<D>(p, cd, head, 2, plan, kh2, wave);
-  dma_v<D>(p, cd, head, 0, plan, vbuf0, wave);
+  Cursor kcur = cursor_at(p, cd, 0), vcur = kcur;
+  dma_k<D>(p, head, kcur, plan, kh0, wave);
+  advance(p, kcur, HK);
+  if (nh > 1) dma_k<D>(p, head, kcur, plan, kh1, wave);
+  advance(p, kcur, HK);
+  if (nh > 2) dma_k<D>(p, head, kcur, plan, kh2, wave);
+  advance(p, kcur, HK);
+  dma_v<D>(p, head, vcur, plan, vbuf0, wave);
+  advance(p, vcur, BN);
 
   bf16x8 qf[KS];
   {
@@ -836,7 +866,7 @@ __global__ __launch_bounds__(NTD, 2) void attn_fwd_dma_kernel(const AttnParams p
   for (int i = 0; i < 16; ++i) sa[i] = 0.f;
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    const bf16x8 kf = *(const bf16x8*)(kh0 + kx[ks & 3] + (ks >> 2) * 128);
+    const bf16x8 kf = *(const bf16x8*)(kh0 + kx + 32 * ks);
     sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sa, 0, 0, 0);
   }
   float m;
@@ -864,18 +894,21 @@ __global__ __launch_bounds__(NTD, 2) void attn_fwd_dma_kernel(const AttnParams p
     char* const k_f1 = even ? kh0 : kh2;  // receives half-tile 2j+4
     char* const vb_cur = even ? vbuf0 : vbuf1;
     char* const vb_free = even ? vbuf1 : vbuf0;
-    if (2 * j + 3 < nh) dma_k<D>(p, cd, head, 2 * j + 3, plan, k_f0, wave);
-    if (2 * j + 4 < nh) dma_k<D>(p, cd, head, 2 * j + 4, plan, k_f1, wave);
-    if (j + 1 < nt) dma_v<D>(p, cd, head, j + 1, plan, vb_free, wave);
+    if (2 * j + 3 < nh) dma_k<D>(p, head, kcur, plan, k_f0, wave);
+    advance(p, kcur, HK);
+    if (2 * j + 4 < nh) dma_k<D>(p, head, kcur, plan, k_f1, wave);
+    advance(p, kcur, HK);
+    if (j + 1 < nt) dma_v<D>(p, head, vcur, plan, vb_free, wave);
+    advance(p, vcur, BN);
     if (j > 0 && edge(j)) {
       zero_v_outside<D>(vb_cur, j, lo, hi);
       __syncthreads();
     }
-    float mx = half_step<D, decltype(m0_tag)::value>(sa, sb, o, qf, k_a, vb_cur, kx, vx[0][0], vx[0][1], m, l,
+    float mx = half_step<D, decltype(m0_tag)::value>(sa, sb, o, qf, k_a, vb_cur, kx, vx0, m, l,
                                                      sl2, (2 * j + 1) * HK, lo, hi, hf);
     if (2 * j + 1 < nh) {
       maybe_rescale<D>(mx, m, l, o);
-      mx = half_step<D, decltype(m1_tag)::value>(sb, sa, o, qf, k_b, vb_cur, kx, vx[1][0], vx[1][1], m, l,
+      mx = half_step<D, decltype(m1_tag)::value>(sb, sa, o, qf, k_b, vb_cur, kx, vx1, m, l,
                                                  sl2, (2 * j + 2) * HK, lo, hi, hf);
       if (2 * j + 2 < nh) maybe_rescale<D>(mx, m, l, o);
     }
