@@ -580,49 +580,66 @@ __device__ __forceinline__ void dma16(const void* src, void* lds) {
                                    (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
 }
 
-// Scalar cursor over the chunk's keys for one DMA stream: ring slot and
-// in-page offset of the next run to load.  A run (32 or 64 keys) spans at
-// most two pages (pages hold >= 64 keys).  For key k of the run (0-based),
-// the K row is at byte (k < split ? kb0 : kb1) + k * 2D and the V^T column at
+// Scalar cursor over the chunk's keys for one DMA stream (K half-tiles or
+// V^T tiles): ring slot and in-page offset of the next run, plus the byte
+// bases of the (page, head) blocks of that slot (b0) and of the next slot (b1)
+// in both the K and the V cache.  A run (32 or 64 keys) spans at most two
+// pages (pages hold >= 64 keys).  For key k of the run (0-based), the K row is
+// at byte (k < split ? kb0 : kb1) + k * 2D and the V^T column at
 // (k < split ? vb0 : vb1) + d * P * 2 + k * 2, relative to the cache bases;
-// kb1 / vb1 are biased by -P so one formula serves both pages.
+// kb1 / vb1 are biased by -P so one formula serves both pages.  The bases are
+// refreshed only when the cursor crosses into the next page.
 struct Cursor {
   int32_t slot, off;
+  uint32_t k0, k1, v0, v1;
 };
 struct RunGeom {
   uint32_t kb0, kb1, vb0, vb1;
   int32_t split;
 };
 
-__device__ __forceinline__ Cursor cursor_at(const AttnParams& p, const ChunkDesc& cd, int rel0) {
+template <int D>
+__device__ __forceinline__ void slot_bases(const AttnParams& p, int head, int slot, uint32_t& kb, uint32_t& vb) {
+  const uint32_t r = (uint32_t)(p.table[slot] * p.H + head);
+  kb = r * (uint32_t)p.P * (2 * D);
+  vb = r * (uint32_t)p.P * (2 * D);  // V^T block of (page, head): D rows of P keys, same size as K's
+}
+
+__device__ __forceinline__ int next_slot(const AttnParams& p, int s) { return s + 1 == p.T ? 0 : s + 1; }
+
+template <int D>
+__device__ __forceinline__ Cursor cursor_at(const AttnParams& p, const ChunkDesc& cd, int head, int rel0) {
   const uint32_t x = (uint32_t)cd.map.base_off + (uint32_t)rel0;
   const uint32_t pg = fastdiv(x, p.divP);
   Cursor c;
   c.off = (int32_t)(x - pg * p.divP.d);
-  uint32_t slot = (uint32_t)cd.map.base_slot + pg;
+  const uint32_t slot = (uint32_t)cd.map.base_slot + pg;
   c.slot = (int32_t)(slot - fastdiv(slot, p.divT) * p.divT.d);
+  slot_bases<D>(p, head, c.slot, c.k0, c.v0);
+  slot_bases<D>(p, head, next_slot(p, c.slot), c.k1, c.v1);
   return c;
 }
 
 template <int D>
-__device__ __forceinline__ RunGeom run_geom(const AttnParams& p, int head, const Cursor& c) {
-  const int slot1 = c.slot + 1 == p.T ? 0 : c.slot + 1;
-  const uint32_t b0 = (uint32_t)(p.table[c.slot] * p.H + head), b1 = (uint32_t)(p.table[slot1] * p.H + head);
-  const uint32_t P = (uint32_t)p.P;
+__device__ __forceinline__ RunGeom run_geom(const AttnParams& p, const Cursor& c) {
   RunGeom g;
   g.split = p.P - c.off;
-  g.kb0 = (b0 * P + (uint32_t)c.off) * (2 * D);
-  g.kb1 = (b1 * P + (uint32_t)c.off - P) * (2 * D);
-  g.vb0 = (b0 * (uint32_t)D * P + (uint32_t)c.off) * 2;
-  g.vb1 = (b1 * (uint32_t)D * P + (uint32_t)c.off - P) * 2;
+  g.kb0 = c.k0 + (uint32_t)c.off * (2 * D);
+  g.kb1 = c.k1 + (uint32_t)(c.off - p.P) * (2 * D);
+  g.vb0 = c.v0 + (uint32_t)c.off * 2;
+  g.vb1 = c.v1 + (uint32_t)(c.off - p.P) * 2;
   return g;
 }
 
-__device__ __forceinline__ void advance(const AttnParams& p, Cursor& c, int n) {
+template <int D>
+__device__ __forceinline__ void advance(const AttnParams& p, int head, Cursor& c, int n) {
   c.off += n;
   if (c.off >= p.P) {
     c.off -= p.P;
-    c.slot = c.slot + 1 == p.T ? 0 : c.slot + 1;
+    c.slot = next_slot(p, c.slot);
+    c.k0 = c.k1;
+    c.v0 = c.v1;
+    slot_bases<D>(p, head, next_slot(p, c.slot), c.k1, c.v1);
   }
 }
 
@@ -665,10 +682,10 @@ __device__ __forceinline__ DmaPlan<D> make_plan(int wave, int lane, int P) {
 
 // DMA the K half-tile at cursor c (32 keys) into khalf.
 template <int D>
-__device__ __forceinline__ void dma_k(const AttnParams& p, int head, const Cursor& c, const DmaPlan<D>& pl,
-                                      char* khalf, int wave) {
+__device__ __forceinline__ void dma_k(const AttnParams& p, const Cursor& c, const DmaPlan<D>& pl, char* khalf,
+                                      int wave) {
   using G = Geo<D>;
-  const RunGeom g = run_geom<D>(p, head, c);
+  const RunGeom g = run_geom<D>(p, c);
 #pragma unroll
   for (int r = 0; r < G::KPW; ++r) {
     if (wave + NW * r < G::KDMA) {
@@ -680,10 +697,10 @@ __device__ __forceinline__ void dma_k(const AttnParams& p, int head, const Curso
 
 // DMA the V^T tile at cursor c (64 keys) into vbuf.
 template <int D>
-__device__ __forceinline__ void dma_v(const AttnParams& p, int head, const Cursor& c, const DmaPlan<D>& pl,
-                                      char* vbuf, int wave) {
+__device__ __forceinline__ void dma_v(const AttnParams& p, const Cursor& c, const DmaPlan<D>& pl, char* vbuf,
+                                      int wave) {
   using G = Geo<D>;
-  const RunGeom g = run_geom<D>(p, head, c);
+  const RunGeom g = run_geom<D>(p, c);
 #pragma unroll
   for (int r = 0; r < G::VPW; ++r) {
     if (wave + NW * r < G::VDMA) {
@@ -824,15 +841,15 @@ __global__ __launch_bounds__(NTD, 2) void attn_fwd_dma_kernel(const AttnParams p
   const int vx1 = lq * G::VROW + 16 * (4 + 2 * hf);  // ... keys 32 + 16 hf .. (second half)
 
   // K half-tiles 0..2 and V tile 0 in flight while Q is fetched
-  Cursor kcur = cursor_at(p, cd, 0), vcur = kcur;
-  dma_k<D>(p, head, kcur, plan, kh0, wave);
-  advance(p, kcur, HK);
-  if (nh > 1) dma_k<D>(p, head, kcur, plan, kh1, wave);
-  advance(p, kcur, HK);
-  if (nh > 2) dma_k<D>(p, head, kcur, plan, kh2, wave);
-  advance(p, kcur, HK);
-  dma_v<D>(p, head, vcur, plan, vbuf0, wave);
-  advance(p, vcur, BN);
+  Cursor kcur = cursor_at<D>(p, cd, head, 0), vcur = kcur;
+  dma_k<D>(p, kcur, plan, kh0, wave);
+  advance<D>(p, head, kcur, HK);
+  if (nh > 1) dma_k<D>(p, kcur, plan, kh1, wave);
+  advance<D>(p, head, kcur, HK);
+  if (nh > 2) dma_k<D>(p, kcur, plan, kh2, wave);
+  advance<D>(p, head, kcur, HK);
+  dma_v<D>(p, vcur, plan, vbuf0, wave);
+  advance<D>(p, head, vcur, BN);
 
   bf16x8 qf[KS];
   {
@@ -851,12 +868,10 @@ __global__ __launch_bounds__(NTD, 2) void attn_fwd_dma_kernel(const AttnParams p
     for (int i = 0; i < 16; ++i) o[b][i] = 0.f;
   float l = 0.f;
 
-  auto edge = [&](int t) { return t * BN < lo || t * BN + BN > hi; };    // 64-key tile t
-  auto hedge = [&](int q) { return q * HK < lo || q * HK + HK > hi; };  // 32-key half-tile q
 
   wait_vmcnt<0>();
   __syncthreads();
-  if (edge(0)) {
+  if (lo > 0 || BN > hi) {  // tile 0 is an edge tile
     zero_v_outside<D>(vbuf0, 0, lo, hi);
     __syncthreads();
   }
@@ -894,13 +909,13 @@ __global__ __launch_bounds__(NTD, 2) void attn_fwd_dma_kernel(const AttnParams p
     char* const k_f1 = even ? kh0 : kh2;  // receives half-tile 2j+4
     char* const vb_cur = even ? vbuf0 : vbuf1;
     char* const vb_free = even ? vbuf1 : vbuf0;
-    if (2 * j + 3 < nh) dma_k<D>(p, head, kcur, plan, k_f0, wave);
-    advance(p, kcur, HK);
-    if (2 * j + 4 < nh) dma_k<D>(p, head, kcur, plan, k_f1, wave);
-    advance(p, kcur, HK);
-    if (j + 1 < nt) dma_v<D>(p, head, vcur, plan, vb_free, wave);
-    advance(p, vcur, BN);
-    if (j > 0 && edge(j)) {
+    if (2 * j + 3 < nh) dma_k<D>(p, kcur, plan, k_f0, wave);
+    advance<D>(p, head, kcur, HK);
+    if (2 * j + 4 < nh) dma_k<D>(p, kcur, plan, k_f1, wave);
+    advance<D>(p, head, kcur, HK);
+    if (j + 1 < nt) dma_v<D>(p, vcur, plan, vb_free, wave);
+    advance<D>(p, head, vcur, BN);
+    if (j > 0 && 64 * j + 64 > hi) {  // edge tile (tile 0 was handled before the loop)
       zero_v_outside<D>(vb_cur, j, lo, hi);
       __syncthreads();
     }
@@ -917,9 +932,11 @@ __global__ __launch_bounds__(NTD, 2) void attn_fwd_dma_kernel(const AttnParams p
   };
   using T_ = std::true_type;
   using F_ = std::false_type;
+  // Half-tiles q >= 1 need masking iff they reach past hi (lo < 8 only affects
+  // half-tile 0, masked before the loop): iff q >= qe.
+  const int qe = hi / HK;
   auto dispatch = [&](auto even_tag, int j) {
-    const bool e1 = hedge(2 * j + 1), e2 = hedge(2 * j + 2);
-    if (!e1 && !e2)
+    if (2 * j + 2 < qe)
       step(even_tag, F_{}, F_{}, j);
     else
       step(even_tag, T_{}, T_{}, j);
