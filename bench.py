@@ -13,9 +13,10 @@ Prints one JSON line.  Inputs are synthetic (seeded on the device) and already
 resident in HBM when the timed region starts.
 """
 import argparse
+import hashlib
 import json
-import math
 import os
+import re
 import sys
 import time
 
@@ -52,7 +53,41 @@ def parse():
     ap.add_argument("--workload", default="round", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=4680, help="query rows in the oracle timing sample")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="after the timed run, copy a buffer of this many MiB once (a plain copy kernel of "
+                         "known size that scales the FETCH_SIZE / WRITE_SIZE counters of a profiled run)")
     return ap.parse_args()
+
+
+def kernel_of(dtype):
+    """Attention kernel the library launches for a workload (the dispatch rule of wf_chunk_attn_fwd:
+    bf16 caches with pages of >= 64 tokens take the LDS-DMA kernel, E4M3FN caches the staged one)."""
+    return "attn_fwd_dma_kernel<128>" if dtype == "bf16" else "attn_fwd_bf16_kernel<128, true>"
+
+
+def source_sha(name):
+    with open(os.path.join(ROOT, "chunk_causal_dit_wf_amd", "csrc", name), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def hbm_traffic(kernel, workload, source):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary
+    (FETCH_SIZE and WRITE_SIZE, each scaled by a plain copy of known size).  None when no summary
+    exists or the kernel source changed after the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "%s_%s_hbm_traffic.md" % (kernel, workload))
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    sha = re.search(r"^source_sha256: *([0-9a-f]{64})", txt, re.M)
+    val = re.search(r"^hbm_bytes_per_launch: *([0-9.eE+]+)", txt, re.M)
+    if sha is None or val is None or sha.group(1) != source_sha(source):
+        return None
+    return float(val.group(1))
+
+
+def pct(xs, q):
+    ys = sorted(xs)
+    return ys[min(len(ys) - 1, max(0, int(round(q * (len(ys) - 1)))))]
 
 
 class Layer:
@@ -161,8 +196,8 @@ def run_round(args, cfg):
     avg_app = sum(app_ms) / len(app_ms)
     return dict(
         ms_per_step=ms_step, wall_s=wall, value=total_flops / (total_ms * 1e-3) / 1e12,
-        attn_kernel_ms=avg_att, attn_tflops=flops_per_launch / (avg_att * 1e-3) / 1e12,
-        append_kernel_ms=avg_app, append_gbps=app_bytes / (avg_app * 1e-3) / 1e9,
+        attn_kernel_ms=avg_att, attn_tflops=flops_per_launch / (avg_att * 1e-3) / 1e12, att_ms=att_ms,
+        append_kernel_ms=avg_app, append_gbps=app_bytes / (avg_app * 1e-3) / 1e9, app_ms=app_ms,
         chunks_per_s=1000.0 / ms_step, flops_per_launch=flops_per_launch, append_bytes=app_bytes,
         H=H, D=D, layers=cfg["layers"])
 
@@ -203,8 +238,19 @@ def run_single(args, cfg, wave):
     ms = [a.elapsed_time(b) for a, b in evs]
     avg = sum(ms) / len(ms)
     return dict(ms_per_step=avg, wall_s=wall, value=flops / (avg * 1e-3) / 1e12, attn_kernel_ms=avg,
-                attn_tflops=flops / (avg * 1e-3) / 1e12, flops_per_launch=flops, H=H, D=D, layers=1,
-                append_kernel_ms=None, append_gbps=None, chunks_per_s=None, append_bytes=None)
+                attn_tflops=flops / (avg * 1e-3) / 1e12, flops_per_launch=flops, H=H, D=D, layers=1, att_ms=ms,
+                append_kernel_ms=None, append_gbps=None, chunks_per_s=None, append_bytes=None, app_ms=None)
+
+
+def calib_copy(mib):
+    """One plain device copy of `mib` MiB (read mib, write mib): the reference kernel for counter scaling."""
+    import torch
+    x = torch.ones(mib * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    y.copy_(x)
+    torch.cuda.synchronize()
+    del x, y
 
 
 def cpu_baseline(rows, H, D, keys):
@@ -245,6 +291,10 @@ def main():
     else:
         r = run_single(args, cfg, wave=args.workload == "wave")
     peak = FP8_PEAK_TFLOPS if cfg["dtype"] == "fp8" else BF16_PEAK_TFLOPS
+    kernel = kernel_of(cfg["dtype"])
+    kname = kernel.split("<")[0]
+    traffic = hbm_traffic(kname, args.workload, "attn_fwd.hip")
+    att = r["att_ms"]
     out = {
         "metric": METRIC,
         "value": round(r["value"], 3),
@@ -264,18 +314,24 @@ def main():
         "pct_bf16_peak": round(100.0 * r["value"] / BF16_PEAK_TFLOPS, 2),
         "attn_kernel_tflops": round(r["attn_tflops"], 2),
         "attn_kernel_ms": round(r["attn_kernel_ms"], 4),
+        "attn_kernel_ms_p10_p50_p90": [round(pct(att, q), 4) for q in (0.1, 0.5, 0.9)],
         "kv_append_GBps": None if r["append_gbps"] is None else round(r["append_gbps"], 1),
         "append_kernel_ms": None if r["append_kernel_ms"] is None else round(r["append_kernel_ms"], 5),
         "chunks_per_s": None if r["chunks_per_s"] is None else round(r["chunks_per_s"], 3),
         "roofline": {"bound": "mfma", "achieved": round(r["attn_tflops"], 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(r["attn_tflops"] / peak, 4), "traffic": None,
-                     "kernel": "attn_fwd_bf16_kernel<128,%s>" % ("true" if cfg["dtype"] == "fp8" else "false"),
-                     "flops_per_launch": r["flops_per_launch"]},
+                     "frac": round(r["attn_tflops"] / peak, 4), "traffic": traffic,
+                     "kernel": kernel, "flops_per_launch": r["flops_per_launch"]},
     }
     if r["append_gbps"] is not None:
+        app = r["app_ms"]
+        out["append_kernel_ms_p10_p50_p90"] = [round(pct(app, q), 5) for q in (0.1, 0.5, 0.9)]
         out["append_roofline"] = {"bound": "hbm", "achieved": round(r["append_gbps"], 1), "peak": HBM_PEAK_GBPS,
                                   "unit": "GB/s", "frac": round(r["append_gbps"] / HBM_PEAK_GBPS, 4),
+                                  "traffic": hbm_traffic("append_kernel", args.workload, "kv_cache.hip"),
+                                  "kernel": "append_kernel<%d, 128>" % (2 if cfg["dtype"] == "bf16" else 1),
                                   "bytes_per_launch": r["append_bytes"]}
+    if args.calib_copy_mib > 0:
+        calib_copy(args.calib_copy_mib)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(min(args.cpu_rows, CHUNK), r["H"], r["D"],
                                            WINDOW if "round" in args.workload else 4 * CHUNK)
