@@ -187,12 +187,17 @@ wf_status wf_kv_append(wf_kv_cache* c, int64_t pos, int32_t n, const void* k_new
   p.T = c->table_len;
   p.nblk = nblk;
   p.esize = es;
-  p.lead = (int32_t)(pos % 64);
+  p.lead = (int32_t)(pos % c->page_size);
   p.map = page_map(c, pos - p.lead);
-  p.divP = wf::make_fastdiv((uint32_t)c->page_size);
+  const int64_t tpp = (c->page_size + 63) / 64;
+  p.div_tpp = wf::make_fastdiv((uint32_t)tpp);
+  p.divH = wf::make_fastdiv((uint32_t)c->num_heads);
   p.divT = wf::make_fastdiv((uint32_t)c->table_len);
   std::memcpy(p.table, c->page_table, sizeof(int32_t) * c->table_len);
-  const int ntiles = (p.lead + n + 63) / 64;
+  const int64_t npages = ((int64_t)p.lead + n + c->page_size - 1) / c->page_size;
+  if (npages * tpp * c->num_heads >= ((int64_t)1 << 31) || (int64_t)p.lead + n + 64 >= ((int64_t)1 << 31))
+    return fail(WF_ERR_UNSUPPORTED, "append of %d tokens needs too many tiles", n);
+  const int ntiles = (int)(npages * tpp);
   hipError_t e = wf::launch_append(p, ntiles, (hipStream_t)stream);
   if (e != hipSuccess) return fail(WF_ERR_HIP, "append launch failed: %s", hipGetErrorString(e));
   c->end = std::max(c->end, pos + n);

@@ -59,9 +59,11 @@ struct AppendParams {
   int32_t n;              // tokens
   int32_t H, D, P, T, nblk;
   int32_t esize;          // bytes per element (4, 2, 1)
-  int32_t lead;           // (pos mod 64): index of the first token inside tile 0
-  PageMap map;            // for logical base = pos - lead (64-aligned)
-  FastDiv divP, divT;
+  int32_t lead;           // pos mod P: page offset of the first appended token
+  PageMap map;            // for logical base = pos - lead (the start of pos's page)
+  FastDiv div_tpp;        // tiles per page, ceil(P / 64)
+  FastDiv divH;           // heads
+  FastDiv divT;
   int32_t table[WF_MAX_TABLE_LEN];
 };
 
