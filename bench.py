@@ -38,6 +38,9 @@ WORKLOADS = {
     "fp8round": dict(layers=40, H=40, D=128, dtype="fp8", std=1.0,
                      name="14b forward round: 40 layers x (evict + append 4680 tok + attend 4680 q x 32760 k), "
                           "H40 D128 bf16 Q / e4m3 K,V, paged ring P1560 T21"),
+    "frameround": dict(layers=30, H=12, D=128, dtype="bf16", std=0.5, chunk=FRAME,
+                       name="wan1.3b frame-wise round: 30 layers x (evict + append 1560 tok + attend 1560 q x "
+                            "32760 k), H12 D128 bf16, paged ring P1560 T21"),
     "call": dict(layers=1, H=12, D=128, dtype="bf16", std=0.5,
                  name="wan1.3b single call: 4680 q x 18720 k, H12 D128 bf16"),
     "wave": dict(layers=1, H=12, D=128, dtype="bf16", std=0.5,
@@ -53,6 +56,9 @@ def parse():
     ap.add_argument("--workload", default="round", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=4680, help="query rows in the oracle timing sample")
+    ap.add_argument("--schedule", default="balanced", choices=["balanced", "tile"],
+                    help="attention schedule: balanced shares of (query tile x key tile) steps with a "
+                         "merge of split tiles (needs a workspace), or one workgroup per query tile")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the timed run, copy a buffer of this many MiB once (a plain copy kernel of "
                          "known size that scales the FETCH_SIZE / WRITE_SIZE counters of a profiled run)")
@@ -95,18 +101,19 @@ class Layer:
 
     def __init__(self, wf, torch, synth, cfg, layer, gen):
         H, D, dt = cfg["H"], cfg["D"], cfg["dtype"]
+        n = cfg.get("chunk", CHUNK)
         table = synth.permuted_table(synth.W_WAN_ROUND if dt == "bf16" else synth.W_14B_FP8, layer, 21)
         self.cache = wf.KVCache(21, FRAME, H, D, dt, table.tolist(), device="cuda")
         std = cfg["std"]
-        self.q = (torch.randn((CHUNK, H, D), generator=gen, device="cuda") * std).to(torch.bfloat16)
+        self.q = (torch.randn((n, H, D), generator=gen, device="cuda") * std).to(torch.bfloat16)
         self.o = torch.empty_like(self.q)
         if dt == "bf16":
-            self.k = (torch.randn((CHUNK, H, D), generator=gen, device="cuda") * std).to(torch.bfloat16)
-            self.v = (torch.randn((CHUNK, H, D), generator=gen, device="cuda") * std).to(torch.bfloat16)
+            self.k = (torch.randn((n, H, D), generator=gen, device="cuda") * std).to(torch.bfloat16)
+            self.v = (torch.randn((n, H, D), generator=gen, device="cuda") * std).to(torch.bfloat16)
             self.ks = self.vs = None
         else:
-            self.k, self.ks = quantize_dev(torch, torch.randn((CHUNK, H, D), generator=gen, device="cuda") * std)
-            self.v, self.vs = quantize_dev(torch, torch.randn((CHUNK, H, D), generator=gen, device="cuda") * std)
+            self.k, self.ks = quantize_dev(torch, torch.randn((n, H, D), generator=gen, device="cuda") * std)
+            self.v, self.vs = quantize_dev(torch, torch.randn((n, H, D), generator=gen, device="cuda") * std)
 
 
 def quantize_dev(torch, x):
@@ -139,19 +146,21 @@ def run_round(args, cfg):
     gen.manual_seed(synth.SEED)
     layers = [Layer(wf, torch, synth, cfg, l, gen) for l in range(cfg["layers"])]
     H, D = cfg["H"], cfg["D"]
-    # prefill 18 frames (6 chunks) per layer with the layer's chunk data
+    n = cfg.get("chunk", CHUNK)
+    # prefill 18 frames per layer with the layer's chunk data
     for L in layers:
-        for c in range(6):
-            wf.wf_kv_append(L.cache, c * CHUNK, L.k, L.v, L.ks, L.vs)
+        for c in range(18 * FRAME // n):
+            wf.wf_kv_append(L.cache, c * n, L.k, L.v, L.ks, L.vs)
     torch.cuda.synchronize()
     ev = lambda: torch.cuda.Event(enable_timing=True)
+    ws = wf.workspace_for(layers[0].cache, "cuda") if args.schedule == "balanced" else None
 
     def step(record):
         marks = []
         for L in layers:
             c = L.cache
-            if c.end - c.start + CHUNK > c.capacity:
-                wf.wf_kv_evict(c, CHUNK)
+            if c.end - c.start + n > c.capacity:
+                wf.wf_kv_evict(c, n)
             e0 = ev() if record else None
             if record:
                 e0.record()
@@ -160,7 +169,7 @@ def run_round(args, cfg):
             if record:
                 e1.record()
             kb = max(c.start, c.end - WINDOW)
-            wf.wf_chunk_attn_fwd(c, L.q, [0, CHUNK], [kb], [c.end], o=L.o)
+            wf.wf_chunk_attn_fwd(c, L.q, [0, n], [kb], [c.end], o=L.o, workspace=ws)
             if record:
                 e2 = ev()
                 e2.record()
@@ -184,12 +193,12 @@ def run_round(args, cfg):
     app_ms = [a.elapsed_time(b) for a, b, _, _ in all_marks]
     att_ms = [b.elapsed_time(c) for _, b, c, _ in all_marks]
     keys = [k for _, _, _, k in all_marks]
-    flops_per_launch = attn_flops(H, D, CHUNK, keys[0])
+    flops_per_launch = attn_flops(H, D, n, keys[0])
     assert all(k == WINDOW for k in keys)
     esize = 2 if cfg["dtype"] == "bf16" else 1
-    app_bytes = 2 * 2 * CHUNK * H * D * esize
+    app_bytes = 2 * 2 * n * H * D * esize
     if cfg["dtype"] == "fp8":
-        app_bytes += 2 * 2 * (CHUNK // FRAME) * H * (-(-FRAME // 128)) * 4
+        app_bytes += 2 * 2 * (n // FRAME) * H * (-(-FRAME // 128)) * 4
     total_flops = flops_per_launch * len(att_ms)
     ms_step = total_ms / args.steps
     avg_att = sum(att_ms) / len(att_ms)
@@ -224,14 +233,15 @@ def run_single(args, cfg, wave):
     else:
         q_off, kb, ke = [0, CHUNK], [0], [4 * CHUNK]
         flops = attn_flops(H, D, CHUNK, 4 * CHUNK)
+    ws = wf.workspace_for(cache, "cuda") if args.schedule == "balanced" else None
     for _ in range(args.warmup):
-        wf.wf_chunk_attn_fwd(cache, q, q_off, kb, ke, o=o)
+        wf.wf_chunk_attn_fwd(cache, q, q_off, kb, ke, o=o, workspace=ws)
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     t0 = time.perf_counter()
     for a, b in evs:
         a.record()
-        wf.wf_chunk_attn_fwd(cache, q, q_off, kb, ke, o=o)
+        wf.wf_chunk_attn_fwd(cache, q, q_off, kb, ke, o=o, workspace=ws)
         b.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -286,7 +296,7 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     cfg = WORKLOADS[args.workload]
-    if args.workload in ("round", "fp8round"):
+    if args.workload in ("round", "fp8round", "frameround"):
         r = run_round(args, cfg)
     else:
         r = run_single(args, cfg, wave=args.workload == "wave")
@@ -309,8 +319,8 @@ def main():
         "dtype": "bf16" if cfg["dtype"] == "bf16" else "bf16 Q / e4m3 K,V",
         "data": "synthetic (seeded N(0, s^2) on device, random page tables)",
         "config": {"workload": cfg["name"], "layers": cfg["layers"], "heads": r["H"], "head_dim": r["D"],
-                   "query_rows": CHUNK, "keys": WINDOW if "round" in args.workload else None,
-                   "parallelism": "single GPU"},
+                   "query_rows": cfg.get("chunk", CHUNK), "keys": WINDOW if "round" in args.workload else None,
+                   "parallelism": "single GPU", "schedule": args.schedule},
         "pct_bf16_peak": round(100.0 * r["value"] / BF16_PEAK_TFLOPS, 2),
         "attn_kernel_tflops": round(r["attn_tflops"], 2),
         "attn_kernel_ms": round(r["attn_kernel_ms"], 4),

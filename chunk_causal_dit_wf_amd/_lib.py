@@ -67,8 +67,10 @@ def lib():
         L.wf_kv_append.argtypes = [P, i64, i32, vp, vp, vp, vp, vp]
         L.wf_kv_evict.argtypes = [P, i32, ctypes.c_uint32, vp]
         L.wf_chunk_attn_fwd.argtypes = [P, vp, i32, vp, vp, i32, ctypes.POINTER(i32), ctypes.POINTER(i64),
-                                        ctypes.POINTER(i64), f32, vp]
-        for name in ("wf_kv_cache_check", "wf_kv_cache_bytes", "wf_kv_append", "wf_kv_evict", "wf_chunk_attn_fwd"):
+                                        ctypes.POINTER(i64), f32, vp, ctypes.c_uint64, vp]
+        L.wf_chunk_attn_workspace_bytes.argtypes = [P, ctypes.POINTER(ctypes.c_uint64)]
+        for name in ("wf_kv_cache_check", "wf_kv_cache_bytes", "wf_kv_append", "wf_kv_evict", "wf_chunk_attn_fwd",
+                     "wf_chunk_attn_workspace_bytes"):
             getattr(L, name).restype = ctypes.c_int
         L.wf_last_error.restype = ctypes.c_char_p
         L.wf_last_error.argtypes = []
@@ -158,10 +160,35 @@ def wf_kv_evict(cache, n, poison=False, stream=None):
     _check(lib().wf_kv_evict(ctypes.byref(cache.c), int(n), WF_EVICT_POISON if poison else 0, _stream(stream)))
 
 
+def wf_chunk_attn_workspace_bytes(cache):
+    b = ctypes.c_uint64()
+    _check(lib().wf_chunk_attn_workspace_bytes(ctypes.byref(cache.c), ctypes.byref(b)))
+    return b.value
+
+
+_workspaces = {}
+
+
+def workspace_for(cache, device):
+    """A cached device workspace large enough for the balanced schedule (None if the cache needs none).
+    One buffer per device: calls that use it must be ordered on one stream."""
+    n = wf_chunk_attn_workspace_bytes(cache)
+    if n == 0:
+        return None
+    key = torch.device(device)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < n:
+        ws = torch.empty(n, dtype=torch.uint8, device=key)
+        _workspaces[key] = ws
+    return ws
+
+
 def wf_chunk_attn_fwd(cache, q, q_off, kv_begin, kv_end, softmax_scale=0.0, o=None, lse=None,
-                      return_lse=False, stream=None):
+                      return_lse=False, workspace="auto", stream=None):
     """Chunk-wise causal attention.  q: [Nq, H, D] device tensor (f32 or bf16).
 
+    workspace: "auto" (a cached per-device buffer: balanced schedule where the cache dtype uses one),
+    None (one workgroup per query tile) or a uint8 device tensor.
     Returns o (and lse [H, Nq] float32 when return_lse or lse is given).
     """
     nc = len(kv_begin)
@@ -178,8 +205,11 @@ def wf_chunk_attn_fwd(cache, q, q_off, kv_begin, kv_end, softmax_scale=0.0, o=No
         o = torch.empty_like(q)
     if lse is None and return_lse:
         lse = torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32, device=q.device)
+    if isinstance(workspace, str):
+        workspace = workspace_for(cache, q.device) if q.is_cuda else None
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().wf_chunk_attn_fwd(ctypes.byref(cache.c), _ptr(q), qd, _ptr(o), _ptr(lse), nc, qo, kb, ke,
-                                   float(softmax_scale), _stream(stream)))
+                                   float(softmax_scale), _ptr(workspace), wsb, _stream(stream)))
     return (o, lse) if lse is not None else o
 
 

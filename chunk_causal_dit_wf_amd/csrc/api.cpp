@@ -233,9 +233,61 @@ wf_status wf_kv_evict(wf_kv_cache* c, int32_t n, uint32_t flags, void* stream) {
   return ok();
 }
 
+// Split schedule for the DMA kernel (see wf::SplitSched).  Used when every
+// chunk has the same number S of key tiles and there are fewer items than
+// resident blocks: each item's keys are cut into m parts (m items x parts fill
+// the resident blocks, parts of at least kMinPart key tiles), and the blocks
+// still idle take the last b key tiles of q parts each, b chosen so that A and
+// B blocks finish together.  B parts are used only when they take at least
+// 1 / (kMaxQ + 1) of a part: a smaller share does not pay for the extra
+// prologues and partial results, and on a power-limited chip idle CUs are
+// not free capacity (measured: 228 of 256 CUs busy ran at a 3 % higher clock
+// than 254).  Returns false when the plain one-block-per-item schedule is used.
+static bool plan_split(wf::AttnParams& p, int items, int resident) {
+  constexpr int kMinPart = 32;  // key tiles per part
+  constexpr int kMinB = 8;      // key tiles per B part
+  constexpr int kMaxQ = 5;      // B parts per B block
+  constexpr int kMaxParts = 8;  // the merge kernel holds 2 * kMaxParts partials per row
+  const int S = p.chunk[0].nsteps;
+  for (int i = 1; i < p.num_chunks; ++i)
+    if (p.chunk[i].nsteps != S) return false;
+  if (items >= resident) return false;
+  wf::SplitSched sp;
+  sp.S = S;
+  sp.n = items;
+  sp.tiles = items / p.H;
+  sp.m = std::max(1, std::min({resident / items, S / kMinPart, kMaxParts}));
+  const int na = items * sp.m;
+  const int spare = resident - na;
+  sp.b = 0;
+  sp.q = 1;
+  if (spare > 0) {
+    sp.q = (na + spare - 1) / spare;
+    sp.b = (S / sp.m) / (sp.q + 1);
+    if (sp.b < kMinB || sp.q > kMaxQ) sp.b = 0;
+  }
+  if (sp.m == 1 && sp.b == 0) return false;
+  p.sp = sp;
+  return true;
+}
+
+wf_status wf_chunk_attn_workspace_bytes(const wf_kv_cache* c, uint64_t* bytes) {
+  wf_status s = check_layout(c);
+  if (s != WF_OK) return s;
+  if (bytes == nullptr) return fail(WF_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = 0;
+  if (c->kv_dtype != WF_BF16) return ok();
+  int blocks = 0;
+  hipError_t e = wf::attn_dma_resident_blocks(c->head_dim, &blocks);
+  if (e != hipSuccess) return fail(WF_ERR_HIP, "device query failed: %s", hipGetErrorString(e));
+  *bytes = (uint64_t)2 * blocks * wf::ws_slot_floats(c->head_dim) * sizeof(float);
+  return ok();
+}
+
 wf_status wf_chunk_attn_fwd(const wf_kv_cache* c, const void* q, int32_t q_dtype, void* o, float* lse,
                             int32_t num_chunks, const int32_t* q_off, const int64_t* kv_begin,
-                            const int64_t* kv_end, float softmax_scale, void* stream) {
+                            const int64_t* kv_end, float softmax_scale, void* workspace,
+                            uint64_t workspace_bytes, void* stream) {
   wf_status s = check_layout(c);
   if (s != WF_OK) return s;
   if ((s = check_window(c)) != WF_OK) return s;
@@ -268,11 +320,20 @@ wf_status wf_chunk_attn_fwd(const wf_kv_cache* c, const void* q, int32_t q_dtype
   const uint64_t kvb = kv_bytes_of(c);
   if (overlap(o, qb, q, qb) || overlap(o, qb, c->k, kvb) || overlap(o, qb, c->v, kvb))
     return fail(WF_ERR_INVALID_ARG, "o overlaps q or the cache");
+  const uint64_t lb = lse != nullptr ? (uint64_t)nq * c->num_heads * 4 : 0;
   if (lse != nullptr) {
-    const uint64_t lb = (uint64_t)nq * c->num_heads * 4;
     if (overlap(lse, lb, o, qb) || overlap(lse, lb, q, qb) || overlap(lse, lb, c->k, kvb) ||
         overlap(lse, lb, c->v, kvb))
       return fail(WF_ERR_INVALID_ARG, "lse overlaps q, o or the cache");
+  }
+  if ((workspace == nullptr) != (workspace_bytes == 0))
+    return fail(WF_ERR_INVALID_ARG, "workspace and workspace_bytes must both be set or both be 0");
+  if (workspace != nullptr) {
+    if (!aligned(workspace, 256)) return fail(WF_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    if (overlap(workspace, workspace_bytes, q, qb) || overlap(workspace, workspace_bytes, o, qb) ||
+        overlap(workspace, workspace_bytes, c->k, kvb) || overlap(workspace, workspace_bytes, c->v, kvb) ||
+        (lse != nullptr && overlap(workspace, workspace_bytes, lse, lb)))
+      return fail(WF_ERR_INVALID_ARG, "workspace overlaps another argument");
   }
 
   wf::AttnParams p;
@@ -320,6 +381,7 @@ wf_status wf_chunk_attn_fwd(const wf_kv_cache* c, const void* q, int32_t q_dtype
     d.lead = (int32_t)(kv_begin[i] % 8);
     d.nkeys = (int32_t)(kv_end[i] - kv_begin[i]);
     d.map = page_map(c, kv_begin[i] - d.lead);
+    d.nsteps = (int32_t)((d.lead + d.nkeys + 63) / 64);
     items += (int64_t)d.ntiles * c->num_heads;
   }
   p.num_chunks = nc;
@@ -329,9 +391,24 @@ wf_status wf_chunk_attn_fwd(const wf_kv_cache* c, const void* q, int32_t q_dtype
   hipError_t e;
   if (q_dtype == WF_F32)
     e = wf::launch_attn_f32(p, c->head_dim, (hipStream_t)stream);
-  else if (use_dma)
-    e = wf::launch_attn_bf16_dma(p, c->head_dim, (hipStream_t)stream);
-  else if (kvd == WF_BF16)
+  else if (use_dma) {
+    int grid = (int)items;
+    if (workspace != nullptr) {
+      int resident = 0;
+      e = wf::attn_dma_resident_blocks(c->head_dim, &resident);
+      if (e != hipSuccess) return fail(WF_ERR_HIP, "device query failed: %s", hipGetErrorString(e));
+      const uint64_t need = (uint64_t)2 * resident * wf::ws_slot_floats(c->head_dim) * sizeof(float);
+      if (workspace_bytes < need)
+        return fail(WF_ERR_INVALID_ARG, "workspace of %llu bytes is smaller than the %llu required",
+                    (unsigned long long)workspace_bytes, (unsigned long long)need);
+      if (plan_split(p, (int)items, resident)) {
+        p.ws = (float*)workspace;
+        grid = p.sp.n * p.sp.m + (p.sp.b > 0 ? (p.sp.n * p.sp.m + p.sp.q - 1) / p.sp.q : 0);
+      }
+    }
+    e = wf::launch_attn_bf16_dma(p, c->head_dim, grid, (hipStream_t)stream);
+    if (e == hipSuccess && p.ws != nullptr) e = wf::launch_attn_merge(p, c->head_dim, (hipStream_t)stream);
+  } else if (kvd == WF_BF16)
     e = wf::launch_attn_bf16_staged(p, c->head_dim, (hipStream_t)stream);
   else
     e = wf::launch_attn_fp8kv(p, c->head_dim, (hipStream_t)stream);

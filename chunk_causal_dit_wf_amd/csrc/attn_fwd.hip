@@ -804,44 +804,49 @@ __device__ __forceinline__ float half_step(const f32x16& s_cur, f32x16& s_next, 
   return half_max(fmaxf(mx[0], mx[1])) * sl2;
 }
 
+// LDS buffers of the DMA kernel.  K half-tiles form a ring of four, V^T tiles
+// are double-buffered.  They are separate __shared__ objects (see the kernel)
+// so the compiler can tell that DMA into one buffer does not alias reads of
+// another.
+struct Bufs {
+  char *kh0, *kh1, *kh2, *kh3, *vbuf0, *vbuf1;
+};
+
+// One query tile (item) of chunk cd over its 64-key tiles [j0, j1).  slot < 0:
+// the segment is the whole key range and the block writes O (and LSE);
+// otherwise it stores its unnormalised partial result in workspace slot
+// `slot` for the merge kernel.
 template <int D>
-__global__ __launch_bounds__(NTD, 2) void attn_fwd_dma_kernel(const AttnParams p) {
+__device__ __forceinline__ void segment(const AttnParams& p, const ChunkDesc& cd, int qt, int head, int j0,
+                                        int j1, int slot, const Bufs& bf, const DmaPlan<D>& plan, int wave,
+                                        int lane) {
   using G = Geo<D>;
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
-  // K half-tiles in a ring of four; V^T tiles double-buffered.  Separate LDS
-  // objects let the compiler see that DMA into one buffer does not alias
-  // reads of another.
-  __shared__ __align__(1024) char kh0[G::KHALF];
-  __shared__ __align__(1024) char kh1[G::KHALF];
-  __shared__ __align__(1024) char kh2[G::KHALF];
-  __shared__ __align__(1024) char kh3[G::KHALF];
-  __shared__ __align__(1024) char vbuf0[G::VTILE];
-  __shared__ __align__(1024) char vbuf1[G::VTILE];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  char* const kh0 = bf.kh0;
+  char* const kh1 = bf.kh1;
+  char* const kh2 = bf.kh2;
+  char* const kh3 = bf.kh3;
+  char* const vbuf0 = bf.vbuf0;
+  char* const vbuf1 = bf.vbuf1;
   const int lq = lane & 31;  // query column owned by this lane
   const int hf = lane >> 5;  // 32-lane half
-
-  const Item it = decode_item(p, blockIdx.x);
-  const ChunkDesc cd = p.chunk[it.c];
-  const int head = it.head;
-  const int qrow = it.qt * BMD + wave * 32 + lq;
+  const int qrow = qt * BMD + wave * 32 + lq;
   const int row = cd.q_begin + qrow;
   const bool row_ok = qrow < cd.q_len;
-  const int lo = cd.lead, hi = cd.lead + cd.nkeys;
+  // Keys relative to the segment's first tile (logical base kv_begin - lead + 64 j0).
+  const int base = BN * j0;
+  const int lo = max(cd.lead - base, 0);
+  const int hi = min(cd.lead + cd.nkeys, BN * j1) - base;
   const int nt = (hi + BN - 1) / BN;  // 64-key tiles
   const int nh = (hi + HK - 1) / HK;  // 32-key half-tiles
   const float sl2 = p.scale_log2;
-  const DmaPlan<D> plan = make_plan<D>(wave, lane, p.P);
-  const int kx = lq * G::KROW + 16 * hf;          // K row lq, chunk hf (k-step 0)
+  const int kx = lq * G::KROW + 16 * hf;             // K row lq, chunk hf (k-step 0)
   const int vx0 = lq * G::VROW + 16 * (2 * hf);      // V^T row lq, keys 16 hf .. (first half of a tile)
   const int vx1 = lq * G::VROW + 16 * (4 + 2 * hf);  // ... keys 32 + 16 hf .. (second half)
 
   // K half-tiles 0..2 and V tile 0 in flight while Q is fetched
-  Cursor kcur = cursor_at<D>(p, cd, head, 0), vcur = kcur;
+  Cursor kcur = cursor_at<D>(p, cd, head, base), vcur = kcur;
   dma_k<D>(p, kcur, plan, kh0, wave);
   advance<D>(p, head, kcur, HK);
   if (nh > 1) dma_k<D>(p, kcur, plan, kh1, wave);
@@ -867,7 +872,6 @@ __global__ __launch_bounds__(NTD, 2) void attn_fwd_dma_kernel(const AttnParams p
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[b][i] = 0.f;
   float l = 0.f;
-
 
   wait_vmcnt<0>();
   __syncthreads();
@@ -947,18 +951,165 @@ __global__ __launch_bounds__(NTD, 2) void attn_fwd_dma_kernel(const AttnParams p
   }
 
   const float lt = half_sum(l);
-  const float inv = 1.f / lt;
-  if (row_ok) {
-    __bf16* orow = (__bf16*)p.o + ((int64_t)row * p.H + head) * D;
+  if (slot < 0) {
+    const float inv = 1.f / lt;
+    if (row_ok) {
+      __bf16* orow = (__bf16*)p.o + ((int64_t)row * p.H + head) * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          bf16x4 v = {(__bf16)(o[db][4 * g + 0] * inv), (__bf16)(o[db][4 * g + 1] * inv),
+                      (__bf16)(o[db][4 * g + 2] * inv), (__bf16)(o[db][4 * g + 3] * inv)};
+          *(bf16x4*)(orow + db * 32 + 8 * g + 4 * hf) = v;
+        }
+      if (p.lse != nullptr && hf == 0) p.lse[(int64_t)head * p.nq + row] = (m + __log2f(lt)) * kLn2;
+    }
+  } else if (row_ok) {
+    float* ws = p.ws + (int64_t)slot * ws_slot_floats(D);
+    const int r = wave * 32 + lq;
+    float* orow = ws + (int64_t)r * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        bf16x4 v = {(__bf16)(o[db][4 * g + 0] * inv), (__bf16)(o[db][4 * g + 1] * inv),
-                    (__bf16)(o[db][4 * g + 2] * inv), (__bf16)(o[db][4 * g + 3] * inv)};
-        *(bf16x4*)(orow + db * 32 + 8 * g + 4 * hf) = v;
-      }
-    if (p.lse != nullptr && hf == 0) p.lse[(int64_t)head * p.nq + row] = (m + __log2f(lt)) * kLn2;
+      for (int g = 0; g < 4; ++g)
+        *(f32x4*)(orow + db * 32 + 8 * g + 4 * hf) = {o[db][4 * g + 0], o[db][4 * g + 1], o[db][4 * g + 2],
+                                                       o[db][4 * g + 3]};
+    if (hf == 0) {
+      ws[BMD * D + r] = m;
+      ws[BMD * D + BMD + r] = lt;
+    }
+  }
+}
+
+// Split schedule helpers.  Part p of an item covers key tiles [p S / m, (p + 1) S / m).
+__device__ __forceinline__ int part_begin(const SplitSched& sp, int p) { return (int)(((int64_t)p * sp.S) / sp.m); }
+
+// Tile index t (over all chunks, in launch order) and head -> chunk, item.
+__device__ __forceinline__ void tile_item(const AttnParams& p, int t, int head, int& c, int& item) {
+  c = 0;
+  while (c + 1 < p.num_chunks && t * p.H >= p.chunk[c + 1].item0) ++c;
+  item = p.chunk[c].item0 + (t - p.chunk[c].item0 / p.H) * p.H + head;
+}
+
+// Head-major index of the B part of (item, part p): u = (head * m + p) * tiles + tile.
+__device__ __forceinline__ int b_index(const AttnParams& p, int item, int part) {
+  const Item it = decode_item(p, item);
+  const int t = p.chunk[it.c].item0 / p.H + it.qt;
+  return (it.head * p.sp.m + part) * p.sp.tiles + t;
+}
+
+template <int D>
+__global__ __launch_bounds__(NTD, 2) void attn_fwd_dma_kernel(const AttnParams p) {
+  using G = Geo<D>;
+  __shared__ __align__(1024) char kh0[G::KHALF];
+  __shared__ __align__(1024) char kh1[G::KHALF];
+  __shared__ __align__(1024) char kh2[G::KHALF];
+  __shared__ __align__(1024) char kh3[G::KHALF];
+  __shared__ __align__(1024) char vbuf0[G::VTILE];
+  __shared__ __align__(1024) char vbuf1[G::VTILE];
+  const Bufs bf{kh0, kh1, kh2, kh3, vbuf0, vbuf1};
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const DmaPlan<D> plan = make_plan<D>(wave, lane, p.P);
+
+  // Work of this block as a list of (item, key tiles [j0, j1), slot) segments,
+  // walked with one call site so the segment code is inlined once:
+  //   no workspace: item = block, whole key range, final output;
+  //   split schedule, A block: one part of one item, minus the part's tail;
+  //   split schedule, B block: the tails of B parts [u0, u1).
+  const int g = blockIdx.x;
+  const SplitSched& sp = p.sp;
+  const int na = p.ws != nullptr ? sp.n * sp.m : 0;
+  int u = 0, u1 = 1;
+  if (p.ws != nullptr && g >= na) {
+    u = (g - na) * sp.q;
+    u1 = min(u + sp.q, na);
+  }
+  for (; u < u1; ++u) {
+    int item, j0, j1, slot;
+    if (p.ws == nullptr) {
+      item = g;
+      j0 = 0;
+      j1 = p.chunk[decode_item(p, g).c].nsteps;
+      slot = -1;
+    } else if (g < na) {
+      const int part = g / sp.n;
+      item = g - part * sp.n;
+      j0 = part_begin(sp, part);
+      j1 = part_begin(sp, part + 1) - sp.b;
+      slot = g;
+    } else {
+      const int mt = sp.m * sp.tiles;
+      const int head = u / mt;
+      const int rem = u - head * mt;
+      const int part = rem / sp.tiles;
+      int c;
+      tile_item(p, rem - part * sp.tiles, head, c, item);
+      j1 = part_begin(sp, part + 1);
+      j0 = j1 - sp.b;
+      slot = na + u;
+    }
+    const Item it = decode_item(p, item);
+    segment<D>(p, p.chunk[it.c], it.qt, it.head, j0, j1, slot, bf, plan, wave, lane);
+  }
+}
+
+// Merge the partial results of the split schedule: for each row,
+// O = sum_k 2^(m_k - M) O_k / sum_k 2^(m_k - M) l_k with M = max_k m_k (the
+// log-sum-exp combination of attention over disjoint key sets).  One block
+// per (item, kMergeRows rows); the item's partials are its m A parts (slots
+// part * n + item) and, if b > 0, its m B parts.
+template <int D>
+__global__ __launch_bounds__(256) void attn_merge_kernel(const AttnParams p) {
+  constexpr int C4 = D / 4;            // float4 columns per row
+  constexpr int RPP = 256 / C4;        // rows per pass
+  constexpr int MAXP = 16;             // partials held in registers
+  const SplitSched& sp = p.sp;
+  const int nrb = BMD / kMergeRows;
+  const int item = blockIdx.x / nrb;
+  const int r0 = (blockIdx.x - item * nrb) * kMergeRows;
+  const Item it = decode_item(p, item);
+  const ChunkDesc& cd = p.chunk[it.c];
+  const int na = sp.n * sp.m;
+  const int np = sp.b > 0 ? 2 * sp.m : sp.m;
+  int slots[MAXP];
+#pragma unroll
+  for (int k = 0; k < MAXP; ++k) {
+    const int part = k % sp.m;
+    slots[k] = k >= np ? 0 : k < sp.m ? part * sp.n + item : na + b_index(p, item, part);
+  }
+  const int tid = threadIdx.x;
+  const int c4 = tid % C4;
+  const int64_t sf = ws_slot_floats(D);
+  for (int r = r0 + tid / C4; r < r0 + kMergeRows; r += RPP) {
+    const int qrow = it.qt * BMD + r;
+    if (qrow >= cd.q_len) break;
+    float mk[MAXP];
+    float M = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < MAXP; ++k) {
+      mk[k] = k < np ? p.ws[slots[k] * sf + BMD * D + r] : -INFINITY;
+      M = fmaxf(M, mk[k]);
+    }
+    float L = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < MAXP; ++k) {
+      if (k >= np) break;
+      const float* ws = p.ws + slots[k] * sf;
+      const float w = __builtin_amdgcn_exp2f(mk[k] - M);
+      L += w * ws[BMD * D + BMD + r];
+      const f32x4 v = *(const f32x4*)(ws + (int64_t)r * D + 4 * c4);
+      acc += w * v;
+    }
+    const float inv = 1.f / L;
+    const int row = cd.q_begin + qrow;
+    bf16x4 ov = {(__bf16)(acc[0] * inv), (__bf16)(acc[1] * inv), (__bf16)(acc[2] * inv), (__bf16)(acc[3] * inv)};
+    *(bf16x4*)((__bf16*)p.o + ((int64_t)row * p.H + it.head) * D + 4 * c4) = ov;
+    if (p.lse != nullptr && c4 == 0) p.lse[(int64_t)it.head * p.nq + row] = (M + __log2f(L)) * kLn2;
   }
 }
 
@@ -1103,12 +1254,33 @@ hipError_t launch_staged_t(const AttnParams& p, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_attn_bf16_dma(const AttnParams& p, int head_dim, hipStream_t s) {
+hipError_t launch_attn_bf16_dma(const AttnParams& p, int head_dim, int grid, hipStream_t s) {
   if (head_dim == 128)
-    hipLaunchKernelGGL(dma::attn_fwd_dma_kernel<128>, dim3(p.num_items), dim3(dma::NTD), 0, s, p);
+    hipLaunchKernelGGL(dma::attn_fwd_dma_kernel<128>, dim3(grid), dim3(dma::NTD), 0, s, p);
   else
-    hipLaunchKernelGGL(dma::attn_fwd_dma_kernel<64>, dim3(p.num_items), dim3(dma::NTD), 0, s, p);
+    hipLaunchKernelGGL(dma::attn_fwd_dma_kernel<64>, dim3(grid), dim3(dma::NTD), 0, s, p);
   return hipGetLastError();
+}
+
+hipError_t launch_attn_merge(const AttnParams& p, int head_dim, hipStream_t s) {
+  const dim3 grid(p.num_items * (kBlockMDma / kMergeRows));
+  if (head_dim == 128)
+    hipLaunchKernelGGL(dma::attn_merge_kernel<128>, grid, dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL(dma::attn_merge_kernel<64>, grid, dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t attn_dma_resident_blocks(int head_dim, int* blocks) {
+  int dev = 0, cus = 0, per_cu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess)
+    e = head_dim == 128
+            ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, dma::attn_fwd_dma_kernel<128>, dma::NTD, 0)
+            : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, dma::attn_fwd_dma_kernel<64>, dma::NTD, 0);
+  *blocks = cus * (per_cu > 0 ? per_cu : 1);
+  return e;
 }
 
 hipError_t launch_attn_bf16_staged(const AttnParams& p, int head_dim, hipStream_t s) {

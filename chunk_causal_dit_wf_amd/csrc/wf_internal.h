@@ -89,6 +89,25 @@ struct ChunkDesc {
   int32_t lead;      // kv_begin - tile origin (0..7): keys skipped in the first tile
   int32_t nkeys;     // kv_end - kv_begin
   PageMap map;       // for logical base = kv_begin - lead
+  int32_t nsteps;    // 64-key tiles per query tile, ceil((lead + nkeys) / 64)
+};
+
+// Split schedule of the DMA kernel (all chunks with the same nsteps S, fewer
+// items n than resident blocks).  Item i's key tiles are cut into m parts,
+// part p = [p S / m, (p + 1) S / m).  Block g < n m ("A" block) runs part
+// g / n of item g % n minus the part's last b key tiles; those tails ("B"
+// parts, numbered head-major: u = (head * m + p) * tiles + tile) are run q at a
+// time by blocks n m + u / q.  A parts start at the same key for all items of
+// one part index, so blocks of one head stream its K/V in step.  Partial
+// results: A part in slot g, B part u in slot n m + u; a merge kernel combines
+// the 2m (or m) partials of each item.
+struct SplitSched {
+  int32_t m;       // key parts per item (>= 1)
+  int32_t b;       // key tiles moved from the end of every part to B blocks (0: none)
+  int32_t q;       // B parts per B block
+  int32_t n;       // items
+  int32_t tiles;   // query tiles over all chunks (n / H)
+  int32_t S;       // key tiles per item
 };
 
 struct AttnParams {
@@ -104,6 +123,8 @@ struct AttnParams {
   float scale_log2;  // softmax scale * log2(e)
   int32_t num_chunks;
   int32_t num_items;
+  float* ws;             // split schedule: partial results, or null (one block per item)
+  SplitSched sp;
   FastDiv divP, divT;
   ChunkDesc chunk[WF_MAX_CHUNKS];
   int32_t table[WF_MAX_TABLE_LEN];
@@ -114,7 +135,16 @@ constexpr int kBlockMF32 = 128;     // fp32 kernel
 constexpr int kBlockMStaged = 128;  // bf16 Q, register-staged tile loads (E4M3FN or small pages)
 constexpr int kBlockMDma = 256;     // bf16 Q and cache, LDS-DMA tile loads
 
-hipError_t launch_attn_bf16_dma(const AttnParams& p, int head_dim, hipStream_t s);
+// Split schedule: each partial-result slot holds, for the BMD rows of one
+// query tile, the unnormalised O (fp32 [BMD][D]), the reference maximum m
+// (log2 domain) and the row sum l.  At most 2 slots per resident block.
+constexpr int64_t ws_slot_floats(int head_dim) { return (int64_t)kBlockMDma * head_dim + 2 * kBlockMDma; }
+constexpr int kMergeRows = 32;  // query rows per merge block
+
+hipError_t launch_attn_bf16_dma(const AttnParams& p, int head_dim, int grid, hipStream_t s);
+hipError_t launch_attn_merge(const AttnParams& p, int head_dim, hipStream_t s);
+// Blocks of the DMA kernel that can be resident at once on the current device.
+hipError_t attn_dma_resident_blocks(int head_dim, int* blocks);
 hipError_t launch_attn_bf16_staged(const AttnParams& p, int head_dim, hipStream_t s);
 hipError_t launch_attn_f32(const AttnParams& p, int head_dim, hipStream_t s);
 hipError_t launch_attn_fp8kv(const AttnParams& p, int head_dim, hipStream_t s);

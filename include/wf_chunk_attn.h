@@ -152,14 +152,33 @@ wf_status wf_kv_evict(wf_kv_cache *cache, int32_t n, uint32_t flags, void *strea
  *   kv_begin, kv_end   host int64 [num_chunks];
  *              start <= kv_begin[c] < kv_end[c] <= end
  *   softmax_scale      <= 0 selects 1/sqrt(head_dim)
+ *   workspace, workspace_bytes
+ *              optional device scratch (caller-owned, 256-byte aligned, at
+ *              least wf_chunk_attn_workspace_bytes() bytes, not overlapping
+ *              any other argument).  With a workspace, BF16 caches are
+ *              processed by a balanced schedule: the (query tile x key
+ *              tile) work is cut into one equal share per resident
+ *              workgroup, query tiles cut between shares leave fp32 partial
+ *              results in the workspace, and a second kernel merges them by
+ *              their log-sum-exp.  NULL (with workspace_bytes 0) selects one
+ *              workgroup per query tile.  Calls that share a workspace must
+ *              be ordered (same stream).
  * 1 <= num_chunks <= WF_MAX_CHUNKS.  Accumulation is fp32.  Results are
- * deterministic run to run.  Keys outside a chunk's range are never used
- * (NaN there does not leak into the output).
+ * deterministic run to run on a given device and schedule.  Keys outside a
+ * chunk's range are never used (NaN there does not leak into the output).
  */
 wf_status wf_chunk_attn_fwd(const wf_kv_cache *cache, const void *q, int32_t q_dtype, void *o,
                             float *lse, int32_t num_chunks, const int32_t *q_off,
                             const int64_t *kv_begin, const int64_t *kv_end, float softmax_scale,
-                            void *stream);
+                            void *workspace, uint64_t workspace_bytes, void *stream);
+
+/*
+ * Workspace bytes wf_chunk_attn_fwd needs for the balanced schedule on the
+ * current HIP device for caches like `cache` (depends on head_dim and the
+ * device's compute-unit count only; 0 when the cache's dtype does not use
+ * one).  Host only.
+ */
+wf_status wf_chunk_attn_workspace_bytes(const wf_kv_cache *cache, uint64_t *bytes);
 
 /* Text of the last non-OK status on this thread ("" if none). */
 const char *wf_last_error(void);

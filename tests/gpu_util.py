@@ -81,8 +81,8 @@ class Pair:
                 np.array_equal(self.gpu.v_scale.cpu().numpy(), self.ref.v_scale)
         return ok and (self.gpu.start, self.gpu.end) == (self.ref.start, self.ref.end)
 
-    def attend(self, q_dev, q_off, kb, ke, scale=0.0):
-        o, lse = wf.wf_chunk_attn_fwd(self.gpu, q_dev, q_off, kb, ke, scale, return_lse=True)
+    def attend(self, q_dev, q_off, kb, ke, scale=0.0, workspace="auto"):
+        o, lse = wf.wf_chunk_attn_fwd(self.gpu, q_dev, q_off, kb, ke, scale, return_lse=True, workspace=workspace)
         torch.cuda.synchronize()
         return o, lse
 

@@ -158,6 +158,23 @@ def test_attention_validation():
     assert st(q, [0, 16], [20], [30], softmax_scale=float("nan")) == wf.WF_ERR_INVALID_ARG
     assert st(q, [0, 16], [20], [30], o=q) == wf.WF_ERR_INVALID_ARG      # o aliases q
     assert st(q, [0, 0], [20], [30]) == wf.WF_OK                          # no rows: nothing to do
+    ws = torch.zeros(4096, dtype=torch.uint8)
+    assert st(q, [0, 16], [20], [30], workspace=ws[1:]) == wf.WF_ERR_INVALID_ARG   # misaligned workspace
+
+
+def test_attention_workspace_needs_pointer_and_size_together():
+    c = _cache()
+    c.c.start, c.c.end = 0, 200
+    q = torch.zeros(16, 2, 64, dtype=torch.bfloat16)
+    o = torch.zeros_like(q)
+    qo = (ctypes.c_int32 * 2)(0, 16)
+    kb = (ctypes.c_int64 * 1)(0)
+    ke = (ctypes.c_int64 * 1)(100)
+    L = wf.lib()
+    st = L.wf_chunk_attn_fwd(ctypes.byref(c.c), ctypes.c_void_p(q.data_ptr()), wf.WF_BF16,
+                             ctypes.c_void_p(o.data_ptr()), None, 1, qo, kb, ke, 0.0, None, 4096, None)
+    assert st == wf.WF_ERR_INVALID_ARG
+    assert "workspace" in L.wf_last_error().decode()
 
 
 def test_fastdiv_exhaustive_on_host(tmp_path):
