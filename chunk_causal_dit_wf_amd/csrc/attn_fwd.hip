@@ -680,34 +680,50 @@ __device__ __forceinline__ DmaPlan<D> make_plan(int wave, int lane, int P) {
   return pl;
 }
 
-// DMA the K half-tile at cursor c (32 keys) into khalf.
+// DMA the K half-tile at cursor c (32 keys) into khalf.  Runs inside one page
+// (all but about one in P / 32) add the run's byte base to the lane's plan
+// offset; a run that crosses a page selects its page per lane.  Sources are
+// the cache base plus one 32-bit offset per lane (the scalar-base form of the
+// load).
 template <int D>
 __device__ __forceinline__ void dma_k(const AttnParams& p, const Cursor& c, const DmaPlan<D>& pl, char* khalf,
                                       int wave) {
   using G = Geo<D>;
+  if (p.P - c.off >= HK) {
+    const uint32_t soff = c.k0 + (uint32_t)c.off * (2 * D);
+#pragma unroll
+    for (int r = 0; r < G::KPW; ++r)
+      if ((NW - 1) + NW * r < G::KDMA || wave + NW * r < G::KDMA)
+        dma16((const char*)p.k + (soff + pl.koff[r]), khalf + 1024 * (wave + NW * r));
+    return;
+  }
   const RunGeom g = run_geom<D>(p, c);
 #pragma unroll
-  for (int r = 0; r < G::KPW; ++r) {
-    if (wave + NW * r < G::KDMA) {
-      const uint32_t off = (pl.kkey[r] < g.split ? g.kb0 : g.kb1) + pl.koff[r];
-      dma16((const char*)p.k + off, khalf + 1024 * (wave + NW * r));
-    }
-  }
+  for (int r = 0; r < G::KPW; ++r)
+    if (wave + NW * r < G::KDMA)
+      dma16((const char*)p.k + ((pl.kkey[r] < g.split ? g.kb0 : g.kb1) + pl.koff[r]),
+            khalf + 1024 * (wave + NW * r));
 }
 
-// DMA the V^T tile at cursor c (64 keys) into vbuf.
+// DMA the V^T tile at cursor c (64 keys) into vbuf (same scheme as dma_k).
 template <int D>
 __device__ __forceinline__ void dma_v(const AttnParams& p, const Cursor& c, const DmaPlan<D>& pl, char* vbuf,
                                       int wave) {
   using G = Geo<D>;
+  if (p.P - c.off >= BN) {
+    const uint32_t soff = c.v0 + (uint32_t)c.off * 2;
+#pragma unroll
+    for (int r = 0; r < G::VPW; ++r)
+      if ((NW - 1) + NW * r < G::VDMA || wave + NW * r < G::VDMA)
+        dma16((const char*)p.v + (soff + pl.voff[r]), vbuf + 1024 * (wave + NW * r));
+    return;
+  }
   const RunGeom g = run_geom<D>(p, c);
 #pragma unroll
-  for (int r = 0; r < G::VPW; ++r) {
-    if (wave + NW * r < G::VDMA) {
-      const uint32_t off = (pl.vkey[r] < g.split ? g.vb0 : g.vb1) + pl.voff[r];
-      dma16((const char*)p.v + off, vbuf + 1024 * (wave + NW * r));
-    }
-  }
+  for (int r = 0; r < G::VPW; ++r)
+    if (wave + NW * r < G::VDMA)
+      dma16((const char*)p.v + ((pl.vkey[r] < g.split ? g.vb0 : g.vb1) + pl.voff[r]),
+            vbuf + 1024 * (wave + NW * r));
 }
 
 // Zero the keys of V^T tile t (in LDS) that lie outside [lo, hi).
@@ -913,11 +929,16 @@ __device__ __forceinline__ void segment(const AttnParams& p, const ChunkDesc& cd
     char* const k_f1 = even ? kh0 : kh2;  // receives half-tile 2j+4
     char* const vb_cur = even ? vbuf0 : vbuf1;
     char* const vb_free = even ? vbuf1 : vbuf0;
-    if (2 * j + 3 < nh) dma_k<D>(p, kcur, plan, k_f0, wave);
+    // The wave index passes through an empty asm so that the LDS destinations
+    // (one per buffer and instruction) are formed at their use instead of being
+    // hoisted into long-lived scalar registers.
+    int wv = wave;
+    asm volatile("" : "+s"(wv));
+    if (2 * j + 3 < nh) dma_k<D>(p, kcur, plan, k_f0, wv);
     advance<D>(p, head, kcur, HK);
-    if (2 * j + 4 < nh) dma_k<D>(p, kcur, plan, k_f1, wave);
+    if (2 * j + 4 < nh) dma_k<D>(p, kcur, plan, k_f1, wv);
     advance<D>(p, head, kcur, HK);
-    if (j + 1 < nt) dma_v<D>(p, vcur, plan, vb_free, wave);
+    if (j + 1 < nt) dma_v<D>(p, vcur, plan, vb_free, wv);
     advance<D>(p, head, vcur, BN);
     if (j > 0 && 64 * j + 64 > hi) {  // edge tile (tile 0 was handled before the loop)
       zero_v_outside<D>(vb_cur, j, lo, hi);
