@@ -67,8 +67,8 @@ def parse():
 
 def kernel_of(dtype):
     """Attention kernel the library launches for a workload (the dispatch rule of wf_chunk_attn_fwd:
-    bf16 caches with pages of >= 64 tokens take the LDS-DMA kernel, E4M3FN caches the staged one)."""
-    return "attn_fwd_dma_kernel<128>" if dtype == "bf16" else "attn_fwd_bf16_kernel<128, true>"
+    caches with pages of >= 64 tokens take the LDS-DMA kernels, bf16 or fp8 MFMA)."""
+    return "attn_fwd_dma_kernel<128>" if dtype == "bf16" else "attn_fwd_fp8_kernel<128>"
 
 
 def source_sha(name):
@@ -303,7 +303,7 @@ def main():
     peak = FP8_PEAK_TFLOPS if cfg["dtype"] == "fp8" else BF16_PEAK_TFLOPS
     kernel = kernel_of(cfg["dtype"])
     kname = kernel.split("<")[0]
-    traffic = hbm_traffic(kname, args.workload, "attn_fwd.hip")
+    traffic = hbm_traffic(kname, args.workload, "attn_fwd.hip" if cfg["dtype"] == "bf16" else "attn_fp8.hip")
     att = r["att_ms"]
     out = {
         "metric": METRIC,
@@ -316,7 +316,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if cfg["dtype"] == "bf16" else "bf16 Q / e4m3 K,V",
+        "dtype": "bf16" if cfg["dtype"] == "bf16" else "e4m3 (fp8 MFMA; bf16 Q and P quantised in-kernel, e4m3 K,V)",
         "data": "synthetic (seeded N(0, s^2) on device, random page tables)",
         "config": {"workload": cfg["name"], "layers": cfg["layers"], "heads": r["H"], "head_dim": r["D"],
                    "query_rows": cfg.get("chunk", CHUNK), "keys": WINDOW if "round" in args.workload else None,

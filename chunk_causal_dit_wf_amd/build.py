@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libwf_chunk_attn.so")
-SOURCES = ["api.cpp", "kv_cache.hip", "attn_fwd.hip"]
+SOURCES = ["api.cpp", "kv_cache.hip", "attn_fwd.hip", "attn_fp8.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 COMMON = ["-O3", "-fPIC", "-std=c++17", "--offload-arch=" + ARCH, "-I" + os.path.join(ROOT, "include"),

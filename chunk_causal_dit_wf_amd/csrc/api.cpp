@@ -276,9 +276,10 @@ wf_status wf_chunk_attn_workspace_bytes(const wf_kv_cache* c, uint64_t* bytes) {
   if (s != WF_OK) return s;
   if (bytes == nullptr) return fail(WF_ERR_INVALID_ARG, "bytes is NULL");
   *bytes = 0;
-  if (c->kv_dtype != WF_BF16) return ok();
+  if (c->kv_dtype == WF_F32) return ok();
   int blocks = 0;
-  hipError_t e = wf::attn_dma_resident_blocks(c->head_dim, &blocks);
+  hipError_t e = c->kv_dtype == WF_BF16 ? wf::attn_dma_resident_blocks(c->head_dim, &blocks)
+                                        : wf::attn_fp8_resident_blocks(c->head_dim, &blocks);
   if (e != hipSuccess) return fail(WF_ERR_HIP, "device query failed: %s", hipGetErrorString(e));
   *bytes = (uint64_t)2 * blocks * wf::ws_slot_floats(c->head_dim) * sizeof(float);
   return ok();
@@ -359,6 +360,9 @@ wf_status wf_chunk_attn_fwd(const wf_kv_cache* c, const void* q, int32_t q_dtype
   // byte offsets: it takes bf16 caches with pages of at least one tile (64
   // keys) and under 4 GiB.  Everything else goes to the register-staged kernel.
   const bool use_dma = kvd == WF_BF16 && c->page_size >= 64 && kvb < ((uint64_t)1 << 32);
+  bool use_fp8 = kvd == WF_FP8_E4M3 && c->page_size >= 64 && kvb < ((uint64_t)1 << 32);
+  for (int i = 0; i < num_chunks && use_fp8; ++i)
+    use_fp8 = (kv_begin[i] % 8) + (kv_end[i] - kv_begin[i]) <= (int64_t)8 * wf::kFp8MaxGroups;
 
   // Longest-processing-time-first order: chunks with the most (query x key) work are issued first.
   std::vector<int> order;
@@ -369,7 +373,7 @@ wf_status wf_chunk_attn_fwd(const wf_kv_cache* c, const void* q, int32_t q_dtype
     const int64_t wb = (int64_t)(q_off[b + 1] - q_off[b]) * (kv_end[b] - kv_begin[b]);
     return wa > wb;
   });
-  const int block_m = q_dtype == WF_F32 ? wf::kBlockMF32 : use_dma ? wf::kBlockMDma : wf::kBlockMStaged;
+  const int block_m = q_dtype == WF_F32 ? wf::kBlockMF32 : (use_dma || use_fp8) ? wf::kBlockMDma : wf::kBlockMStaged;
   int64_t items = 0;
   int nc = 0;
   for (int i : order) {
@@ -391,11 +395,12 @@ wf_status wf_chunk_attn_fwd(const wf_kv_cache* c, const void* q, int32_t q_dtype
   hipError_t e;
   if (q_dtype == WF_F32)
     e = wf::launch_attn_f32(p, c->head_dim, (hipStream_t)stream);
-  else if (use_dma) {
+  else if (use_dma || use_fp8) {
     int grid = (int)items;
     if (workspace != nullptr) {
       int resident = 0;
-      e = wf::attn_dma_resident_blocks(c->head_dim, &resident);
+      e = use_dma ? wf::attn_dma_resident_blocks(c->head_dim, &resident)
+                  : wf::attn_fp8_resident_blocks(c->head_dim, &resident);
       if (e != hipSuccess) return fail(WF_ERR_HIP, "device query failed: %s", hipGetErrorString(e));
       const uint64_t need = (uint64_t)2 * resident * wf::ws_slot_floats(c->head_dim) * sizeof(float);
       if (workspace_bytes < need)
@@ -406,7 +411,8 @@ wf_status wf_chunk_attn_fwd(const wf_kv_cache* c, const void* q, int32_t q_dtype
         grid = p.sp.n * p.sp.m + (p.sp.b > 0 ? (p.sp.n * p.sp.m + p.sp.q - 1) / p.sp.q : 0);
       }
     }
-    e = wf::launch_attn_bf16_dma(p, c->head_dim, grid, (hipStream_t)stream);
+    e = use_dma ? wf::launch_attn_bf16_dma(p, c->head_dim, grid, (hipStream_t)stream)
+                : wf::launch_attn_fp8_dma(p, c->head_dim, grid, (hipStream_t)stream);
     if (e == hipSuccess && p.ws != nullptr) e = wf::launch_attn_merge(p, c->head_dim, (hipStream_t)stream);
   } else if (kvd == WF_BF16)
     e = wf::launch_attn_bf16_staged(p, c->head_dim, (hipStream_t)stream);

@@ -142,6 +142,11 @@ constexpr int64_t ws_slot_floats(int head_dim) { return (int64_t)kBlockMDma * he
 constexpr int kMergeRows = 32;  // query rows per merge block
 
 hipError_t launch_attn_bf16_dma(const AttnParams& p, int head_dim, int grid, hipStream_t s);
+// E4M3FN cache, fp8 MFMA: pages of >= 64 keys, cache < 4 GiB, and per chunk
+// lead + nkeys <= 8 * kFp8MaxGroups (the per-block scale table in LDS).
+constexpr int kFp8MaxGroups = 8192;
+hipError_t launch_attn_fp8_dma(const AttnParams& p, int head_dim, int grid, hipStream_t s);
+hipError_t attn_fp8_resident_blocks(int head_dim, int* blocks);
 hipError_t launch_attn_merge(const AttnParams& p, int head_dim, hipStream_t s);
 // Blocks of the DMA kernel that can be resident at once on the current device.
 hipError_t attn_dma_resident_blocks(int head_dim, int* blocks);
