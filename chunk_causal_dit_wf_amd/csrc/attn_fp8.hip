@@ -28,6 +28,8 @@
 //
 // Roofline: dense fp8 MFMA.  Algorithmic flops per visible (query, key) pair
 // and head are 4 * head_dim.
+#include <utility>
+
 #include "attn_common.h"
 
 namespace wf {
@@ -178,67 +180,107 @@ __device__ __forceinline__ HalfScale half_scale(const float2* table, int group, 
   return h;
 }
 
-// S^T of one 32-key half-tile: acc = K8 rows (LDS) x Q8 columns (registers).
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// f(integral_constant<int, 0>) ... f(integral_constant<int, N - 1>), unrolled at compile time.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_seq(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_seq(f, std::make_integer_sequence<int, N>{});
+}
+
+// 32 bytes (two 16-byte LDS reads) as an MFMA fp8 operand.
+__device__ __forceinline__ i32x8 lds32(const char* a) {
+  const i32x4 lo = *(const i32x4*)a;
+  const i32x4 hi = *(const i32x4*)(a + 16);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ i32x8 lds16x2(const char* a, int gap) {
+  const i32x4 lo = *(const i32x4*)a;
+  const i32x4 hi = *(const i32x4*)(a + gap);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// MFMA i of a tile's S^T: half-tile i / KS, k-block i % KS.  A operand: 32
+// bytes of LDS row 32 (i / KS) + lq at dims 64 (i % KS) + 32 hf (kx covers lq, hf).
 template <int D>
-__device__ __forceinline__ f32x16 qk_half(const char* krow, const i32x8 (&q8)[Geo<D>::KS]) {
-  f32x16 acc;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-#pragma unroll
-  for (int s = 0; s < Geo<D>::KS; ++s) {
-    const f32x4 lo = *(const f32x4*)(krow + 64 * s);
-    const f32x4 hi = *(const f32x4*)(krow + 64 * s + 16);
-    i32x8 a;
-    a[0] = __float_as_int(lo[0]); a[1] = __float_as_int(lo[1]); a[2] = __float_as_int(lo[2]); a[3] = __float_as_int(lo[3]);
-    a[4] = __float_as_int(hi[0]); a[5] = __float_as_int(hi[1]); a[6] = __float_as_int(hi[2]); a[7] = __float_as_int(hi[3]);
-    acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, q8[s], acc, 0, 0, 0, 0, 0, 0);
-  }
-  return acc;
+__device__ __forceinline__ i32x8 k_frag(const char* kbuf, int kx, int i) {
+  return lds32(kbuf + (i / Geo<D>::KS) * 32 * Geo<D>::KROW + kx + 64 * (i % Geo<D>::KS));
+}
+// PV MFMA db: A operand = V^T row 32 db + lq, keys 16 hf + [0, 16) and 32 + 16 hf + [0, 16).
+template <int D>
+__device__ __forceinline__ i32x8 v_frag(const char* vbuf, int vx, int db) {
+  return lds16x2(vbuf + vx + db * 32 * Geo<D>::VROW, 32);
 }
 
-// Scaled, masked scores of a half-tile in place (edge tiles) and their row max.
-template <bool MASK>
-__device__ __forceinline__ float half_max_scaled(f32x16& acc, const HalfScale& h, int key0, int lo, int hi) {
-  if constexpr (MASK) {
-    float mx = -INFINITY;
+// S^T of one tile in one go (prologue): halves a (keys 0..31) and b (32..63).
+template <int D>
+__device__ __forceinline__ void qk_tile(const char* kbuf, int kx, const i32x8 (&q8)[Geo<D>::KS], f32x16& sa,
+                                        f32x16& sb) {
+  constexpr int KS = Geo<D>::KS;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int key = key0 + i;
-      const float sv = acc[i] * (i < 8 ? h.fa : h.fb);
-      acc[i] = (key >= lo && key < hi) ? sv : -INFINITY;
-      mx = fmaxf(mx, acc[i]);
-    }
-    return mx;
-  } else {
-    float ma = fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3]));
-    ma = fmaxf(ma, fmaxf(fmaxf(acc[4], acc[5]), fmaxf(acc[6], acc[7])));
-    float mb = fmaxf(fmaxf(acc[8], acc[9]), fmaxf(acc[10], acc[11]));
-    mb = fmaxf(mb, fmaxf(fmaxf(acc[12], acc[13]), fmaxf(acc[14], acc[15])));
-    return fmaxf(ma * h.fa, mb * h.fb);
+  for (int i = 0; i < 16; ++i) sa[i] = sb[i] = 0.f;
+#pragma unroll
+  for (int i = 0; i < 2 * KS; ++i) {
+    f32x16& acc = i < KS ? sa : sb;
+    acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(k_frag<D>(kbuf, kx, i), q8[i % KS], acc, 0, 0, 0, 0, 0, 0);
   }
 }
 
-// P' of a half-tile packed to e4m3 (4 dwords) and its contribution to the row
-// sum.  SCALED: acc already holds scaled scores (edge tiles).
-template <bool SCALED>
-__device__ __forceinline__ void half_p(const f32x16& acc, const HalfScale& h, float m, uint32_t (&pk)[4],
-                                       float& l) {
-  const float fa = SCALED ? 1.f : h.fa, fb = SCALED ? 1.f : h.fb;
-  const float ba = h.ca - m, bb = h.cb - m;
-  float sa = 0.f, sb = 0.f;
-  float e[16];
+// Scaled, masked scores of a half-tile in place and their row max (edge tiles).
+__device__ __forceinline__ float mask_half(f32x16& acc, const HalfScale& h, int key0, int lo, int hi) {
+  float mx = -INFINITY;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    e[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[i], i < 8 ? fa : fb, i < 8 ? ba : bb));
-    if (i < 8) sa += e[i]; else sb += e[i];
+    const int key = key0 + i;
+    const float sv = acc[i] * (i < 8 ? h.fa : h.fb);
+    acc[i] = (key >= lo && key < hi) ? sv : -INFINITY;
+    mx = fmaxf(mx, acc[i]);
   }
+  return mx;
+}
+
+// P' of elements [E0, E0 + EN) of a half-tile (EN = 8 or 16, one or two scale
+// groups): exponent, e4m3 packing into pk (dword (E0 + e) / 4 of the half),
+// and the row-sum contribution.  fa, fb: score factors of the two groups (1
+// when acc already holds scaled scores).
+template <int E0, int EN>
+__device__ __forceinline__ void p_group(const f32x16& acc, const HalfScale& h, float fa, float fb, float m,
+                                        uint32_t* pk, float& l) {
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    uint32_t v = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(e[4 * w], e[4 * w + 1], 0, false);
-    v = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(e[4 * w + 2], e[4 * w + 3], (int)v, true);
-    pk[w] = v;
+  for (int g = E0 / 8; g < (E0 + EN) / 8; ++g) {
+    const float f = g == 0 ? fa : fb;
+    const float c = g == 0 ? h.ca : h.cb;
+    const float bias = c - m;
+    float e[8], sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      e[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[8 * g + i], f, bias));
+      sum += e[i];
+    }
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      uint32_t v = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(e[4 * w], e[4 * w + 1], 0, false);
+      v = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(e[4 * w + 2], e[4 * w + 3], (int)v, true);
+      pk[2 * g + w] = v;
+    }
+    l = __builtin_fmaf(sum, __builtin_amdgcn_exp2f(-c), l);
   }
-  l += sa * __builtin_amdgcn_exp2f(-h.ca) + sb * __builtin_amdgcn_exp2f(-h.cb);
+}
+
+// Raw maximum of elements [E0, E0 + EN) of a half-tile (unmasked tiles).
+template <int E0, int EN>
+__device__ __forceinline__ float raw_max(const f32x16& acc) {
+  float m0 = fmaxf(acc[E0], acc[E0 + 1]), m1 = fmaxf(acc[E0 + 2], acc[E0 + 3]);
+#pragma unroll
+  for (int i = E0 + 4; i < E0 + EN; i += 2) {
+    m0 = fmaxf(m0, acc[i]);
+    m1 = fmaxf(m1, acc[i + 1]);
+  }
+  return fmaxf(m0, m1);
 }
 
 struct Bufs {
@@ -344,27 +386,49 @@ __device__ __forceinline__ void segment(const AttnParams& p, const ChunkDesc& cd
     for (int i = 0; i < 16; ++i) o[b][i] = 0.f;
   float l = 0.f;
 
-  const int kx = lq * G::KROW + 32 * hf;                 // K row lq (+ 32 for the second half)
-  const int vx = lq * G::VROW + 16 * hf;                 // V^T row lq, keys 16 hf + [0, 16)
+  const int kx = lq * G::KROW + 32 * hf;  // K row lq, dims 32 hf + [0, 32) of each k-block
+  const int vx = lq * G::VROW + 16 * hf;  // V^T row lq, keys 16 hf + [0, 16)
   wait_vmcnt<0>();
-  __syncthreads();  // tiles 0 and the scale table are in LDS
+  __syncthreads();  // tile 0 and the scale table are in LDS
   if (lo > 0 || TK > hi) {
     zero_v_outside<D>(bf.v0, 0, lo, hi);
     __syncthreads();
   }
-  // S[0] (scaled, masked: tile 0 holds key lo < 8, so the maxima are finite)
-  f32x16 sa = qk_half<D>(bf.k0 + kx, q8), sb = qk_half<D>(bf.k0 + 32 * G::KROW + kx, q8);
-  HalfScale ha = half_scale(bf.scales, 2 * hf, qs), hb = half_scale(bf.scales, 4 + 2 * hf, qs);
-  float m = half_max(fmaxf(half_max_scaled<true>(sa, ha, 16 * hf, lo, hi),
-                           half_max_scaled<true>(sb, hb, 32 + 16 * hf, lo, hi)));
-  bool scaled = true;  // sa, sb hold scaled scores
-  __syncthreads();     // k0 is free for tile 2
+  // S[0], scaled and masked (tile 0 holds key lo < 8, so its row maxima are finite)
+  f32x16 s0a, s0b, s1a, s1b;
+  qk_tile<D>(bf.k0, kx, q8, s0a, s0b);
+  HalfScale h0a = half_scale(bf.scales, 2 * hf, qs), h0b = half_scale(bf.scales, 4 + 2 * hf, qs), h1a, h1b;
+  float m = half_max(fmaxf(mask_half(s0a, h0a, 16 * hf, lo, hi), mask_half(s0b, h0b, 32 + 16 * hf, lo, hi)));
+  __syncthreads();  // k0 is free for tile 2
 
-  for (int j = 0; j < nt; ++j) {
-    char* const kc = (j & 1) ? bf.k0 : bf.k1;   // K[j+1]
-    char* const kf = (j & 1) ? bf.k1 : bf.k0;   // receives K[j+2]
-    char* const vc = (j & 1) ? bf.v1 : bf.v0;   // V[j]
-    char* const vf = (j & 1) ? bf.v0 : bf.v1;   // receives V[j+1]
+  // Step j.  EVEN: S[j] in s0*, S[j+1] computed into s1* (odd j: the other
+  // way).  sc: S[j] holds scaled, masked scores (tile 0, the last tile);
+  // mn: tile j+1 is the last tile and is masked when its maxima are taken.
+  // Both are runtime flags that select factors or take a short uniform
+  // branch, so each parity is instantiated once (more instances of the
+  // staged step exhaust the register file).
+  //   [A] stage i: MFMA i of S[j+1] = K[j+1] Q^T (its fragment read one stage
+  //       ahead) and P' of one 8-key group of S[j] (exp, e4m3 pack, row sum);
+  //   [B] stage d: MFMA d of O += V[j] P[j] and the raw maxima of one group
+  //       of S[j+1]; then the lazy rescale.
+  bool sc = true;
+  auto step = [&](auto even_tag, int j) {
+    constexpr bool even = decltype(even_tag)::value;
+    constexpr int NA = 2 * KS;   // QK MFMAs per tile
+    constexpr int EA = 32 / NA;  // S[j] elements per [A] stage
+    constexpr int EB = 32 / DB;  // S[j+1] elements per [B] stage
+    f32x16& ca = even ? s0a : s1a;
+    f32x16& cb = even ? s0b : s1b;
+    f32x16& na = even ? s1a : s0a;
+    f32x16& nb = even ? s1b : s0b;
+    HalfScale& hca = even ? h0a : h1a;
+    HalfScale& hcb = even ? h0b : h1b;
+    HalfScale& hna = even ? h1a : h0a;
+    HalfScale& hnb = even ? h1b : h0b;
+    char* const kc = even ? bf.k1 : bf.k0;  // K[j+1]
+    char* const kf = even ? bf.k0 : bf.k1;  // receives K[j+2]
+    char* const vc = even ? bf.v0 : bf.v1;  // V[j]
+    char* const vf = even ? bf.v1 : bf.v0;  // receives V[j+1]
     int wv = wave;
     asm volatile("" : "+s"(wv));
     if (j + 2 < nt) dma_k<D>(p, kcur, plan, kf, wv);
@@ -375,54 +439,73 @@ __device__ __forceinline__ void segment(const AttnParams& p, const ChunkDesc& cd
       zero_v_outside<D>(vc, j, lo, hi);
       __syncthreads();
     }
-    // [A] S[j+1] = K[j+1] Q^T  ||  P[j] = exp(S[j])
+    // The last step also computes an S[j+1] (from the stale K buffer, unused):
+    // guarding it would keep two versions of the score registers alive.
     const bool more = j + 1 < nt;
-    f32x16 na, nb;
-    if (more) {
-      na = qk_half<D>(kc + kx, q8);
-      nb = qk_half<D>(kc + 32 * G::KROW + kx, q8);
-    }
-    uint32_t pa[4], pb[4];
-    if (scaled) {
-      half_p<true>(sa, ha, m, pa, l);
-      half_p<true>(sb, hb, m, pb, l);
-    } else {
-      half_p<false>(sa, ha, m, pa, l);
-      half_p<false>(sb, hb, m, pb, l);
-    }
-    // [B] O^T += V^T[j] P^T[j]  ||  row max of S[j+1]
-    i32x8 p8;
-    p8[0] = (int)pa[0]; p8[1] = (int)pa[1]; p8[2] = (int)pa[2]; p8[3] = (int)pa[3];
-    p8[4] = (int)pb[0]; p8[5] = (int)pb[1]; p8[6] = (int)pb[2]; p8[7] = (int)pb[3];
+    const bool mn = more && TK * (j + 1) + TK > hi;
+    const float faa = sc ? 1.f : hca.fa, fab = sc ? 1.f : hca.fb;
+    const float fba = sc ? 1.f : hcb.fa, fbb = sc ? 1.f : hcb.fb;
+    uint32_t pk[8];
+    i32x8 fr[2];
+    fr[0] = k_frag<D>(kc, kx, 0);
+    static_for<NA>([&](auto I) {
+      constexpr int i = decltype(I)::value;
+      if constexpr (i + 1 < NA) fr[(i + 1) & 1] = k_frag<D>(kc, kx, i + 1);
+      f32x16& acc = i < KS ? na : nb;
+      if constexpr (i % KS == 0) {
+        f32x16 z;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const char* vr = vc + vx + db * 32 * G::VROW;
-      const f32x4 lo4 = *(const f32x4*)vr;
-      const f32x4 hi4 = *(const f32x4*)(vr + 32);
-      i32x8 a;
-      a[0] = __float_as_int(lo4[0]); a[1] = __float_as_int(lo4[1]); a[2] = __float_as_int(lo4[2]); a[3] = __float_as_int(lo4[3]);
-      a[4] = __float_as_int(hi4[0]); a[5] = __float_as_int(hi4[1]); a[6] = __float_as_int(hi4[2]); a[7] = __float_as_int(hi4[3]);
-      o[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, p8, o[db], 0, 0, 0, 0, 0, 0);
-    }
-    if (more) {
-      const int g0 = 8 * (j + 1);
-      ha = half_scale(bf.scales, g0 + 2 * hf, qs);
-      hb = half_scale(bf.scales, g0 + 4 + 2 * hf, qs);
-      const int k0 = TK * (j + 1);
-      float mx;
-      scaled = k0 + TK > hi;  // last tile: mask
-      if (scaled)
-        mx = fmaxf(half_max_scaled<true>(na, ha, k0 + 16 * hf, lo, hi),
-                   half_max_scaled<true>(nb, hb, k0 + 32 + 16 * hf, lo, hi));
+        for (int e = 0; e < 16; ++e) z[e] = 0.f;
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fr[i & 1], q8[0], z, 0, 0, 0, 0, 0, 0);
+      } else {
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fr[i & 1], q8[i % KS], acc, 0, 0, 0, 0, 0, 0);
+      }
+      constexpr int e0 = EA * i;
+      if constexpr (e0 < 16)
+        p_group<e0 % 16, EA>(ca, hca, faa, fab, m, pk, l);
       else
-        mx = fmaxf(half_max_scaled<false>(na, ha, 0, lo, hi), half_max_scaled<false>(nb, hb, 0, lo, hi));
+        p_group<e0 % 16, EA>(cb, hcb, fba, fbb, m, pk + 4, l);
+      asm volatile("" : "+v"(l));
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    i32x8 p8;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) p8[w] = (int)pk[w];
+    if (more) {
+      hna = half_scale(bf.scales, 8 * (j + 1) + 2 * hf, qs);
+      hnb = half_scale(bf.scales, 8 * (j + 1) + 4 + 2 * hf, qs);
+    }
+    float gm[4];  // raw maxima of the 8-key groups of S[j+1]: (half a: A, B), (half b: A, B)
+    fr[0] = v_frag<D>(vc, vx, 0);
+    static_for<DB>([&](auto I) {
+      constexpr int d = decltype(I)::value;
+      if constexpr (d + 1 < DB) fr[(d + 1) & 1] = v_frag<D>(vc, vx, d + 1);
+      o[d] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fr[d & 1], p8, o[d], 0, 0, 0, 0, 0, 0);
+#pragma unroll
+      for (int g = EB * d / 8; g < EB * (d + 1) / 8; ++g) {
+        gm[g] = g < 2 ? (g == 0 ? raw_max<0, 8>(na) : raw_max<8, 8>(na))
+                      : (g == 2 ? raw_max<0, 8>(nb) : raw_max<8, 8>(nb));
+      }
+      asm volatile("" : "+v"(o[d]));
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    if (more) {
+      float mx;
+      if (mn)
+        mx = fmaxf(mask_half(na, hna, TK * (j + 1) + 16 * hf, lo, hi),
+                   mask_half(nb, hnb, TK * (j + 1) + 32 + 16 * hf, lo, hi));
+      else
+        mx = fmaxf(fmaxf(gm[0] * hna.fa, gm[1] * hna.fb), fmaxf(gm[2] * hnb.fa, gm[3] * hnb.fb));
       mx = half_max(mx);
       maybe_rescale<D>(mx, m, l, o);
-      sa = na;
-      sb = nb;
     }
+    sc = mn;
     wait_vmcnt<0>();
     __syncthreads();
+  };
+  for (int j = 0; j < nt; j += 2) {
+    step(std::true_type{}, j);
+    if (j + 1 < nt) step(std::false_type{}, j + 1);
   }
 
   const float lt = half_sum(l);
