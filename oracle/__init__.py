@@ -26,12 +26,12 @@ What it computes (plain definitions, float64 throughout):
 Pins that tie these functions to something other than themselves live in
 ``tests/test_oracle_*.py``.  No function here is "parity unpinned".
 """
-from .numerics import decode_bf16, decode_e4m3fn, decode_f32
+from .numerics import decode_bf16, decode_e4m3fn, decode_f32, encode_e4m3fn
 from .attention import chunk_attention, merge_partials
 from .brute import brute_force_attention
 from .cache import KVCacheModel
 
 __all__ = [
-    "decode_bf16", "decode_e4m3fn", "decode_f32",
+    "decode_bf16", "decode_e4m3fn", "decode_f32", "encode_e4m3fn",
     "chunk_attention", "merge_partials", "brute_force_attention", "KVCacheModel",
 ]

@@ -32,10 +32,17 @@ drop the oldest):
         whole.
     evict(n)  needs n <= end - start; start += n.  With poison=True the
         evicted rows are overwritten with NaN codes (a test aid).
+    append_quantized(pos, k_bf16, v_bf16)  (E4M3FN storage) quantises bf16
+        rows page by page and appends codes and scales.  For each page, head
+        and 128-token block: amax = max |x| over the block's tokens and dims
+        (float32), scale = amax / 448 and r = 448 / amax (float32 divisions
+        rounded to nearest; 1 and 1 for an all-zero block), code =
+        E4M3FN(x * r) with the product a float32 multiply rounded to nearest and
+        the conversion rounding to nearest-even with saturation at 448.
 """
 import numpy as np
 
-from .numerics import decode_bf16, decode_e4m3fn, decode_f32
+from .numerics import decode_bf16, decode_e4m3fn, decode_f32, encode_e4m3fn
 
 _STORAGE = {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8}
 _NAN_CODE = {"f32": np.float32(np.nan), "bf16": np.uint16(0x7FC0), "fp8": np.uint8(0x7F)}
@@ -122,6 +129,37 @@ class KVCacheModel:
                 self.k_scale[page] = k_scale_new[j]
                 self.v_scale[page] = v_scale_new[j]
         self.end = max(self.end, pos + n)
+
+    def quantize_pages(self, x_bf16):
+        """bf16 codes [n, H, D] (n a multiple of P) -> E4M3FN codes [n, H, D], scales [n/P, H, nblk]."""
+        x_bf16 = np.asarray(x_bf16)
+        n = x_bf16.shape[0]
+        if n % self.P:
+            raise ValueError("quantised appends must be whole pages")
+        x = decode_bf16(x_bf16).astype(np.float32)  # exact: bf16 values are float32 values
+        codes = np.empty(x.shape, np.uint8)
+        scales = np.empty((n // self.P, self.H, self.nblk), np.float32)
+        f448 = np.float32(448.0)
+        for j in range(n // self.P):
+            for b in range(self.nblk):
+                r0 = j * self.P + b * SCALE_BLOCK
+                r1 = min(r0 + SCALE_BLOCK, (j + 1) * self.P)
+                blk = x[r0:r1]                                       # [rows, H, D] float32
+                amax = np.abs(blk).max(axis=(0, 2))                  # [H] float32
+                pos = amax > 0
+                with np.errstate(divide="ignore", invalid="ignore"):
+                    scale = np.where(pos, amax / f448, np.float32(1.0)).astype(np.float32)
+                    r = np.where(pos, f448 / amax, np.float32(1.0)).astype(np.float32)
+                scales[j, :, b] = scale
+                codes[r0:r1] = encode_e4m3fn(blk * r[None, :, None])  # float32 products
+        return codes, scales
+
+    def append_quantized(self, pos, k_bf16, v_bf16):
+        if self.dtype != "fp8":
+            raise TypeError("append_quantized needs an E4M3FN cache")
+        kc, ks = self.quantize_pages(k_bf16)
+        vc, vs = self.quantize_pages(v_bf16)
+        self.append(pos, kc, vc, ks, vs)
 
     def evict(self, n, poison=False):
         n = int(n)

@@ -47,3 +47,27 @@ def decode_e4m3fn(codes):
     mag = np.where(exp == 0, subnormal, normal)
     mag = np.where((exp == 0xF) & (man == 0x7), np.nan, mag)
     return sign * mag
+
+
+def encode_e4m3fn(x):
+    """float32 values -> OCP E4M3FN codes: round to nearest, ties to even,
+    finite values beyond +-448 saturate to +-448 ("satfinite"), NaN -> 0x7F.
+
+    Written from the format definition (see decode_e4m3fn).  The codes 0x00 ..
+    0x7E enumerate the non-negative finite values in increasing order, so the
+    nearest magnitude is found by bisection over that table; on a tie the code
+    whose mantissa LSB is 0 wins, and for these codes the mantissa LSB is the
+    code's own LSB.  The sign bit is copied, so a negative input that rounds to
+    zero gives 0x80.
+    """
+    x = np.asarray(x, dtype=np.float32)
+    table = decode_e4m3fn(np.arange(0x7F, dtype=np.uint8))  # 0 .. 448, strictly increasing
+    a = np.minimum(np.abs(x).astype(np.float64), 448.0)
+    hi = np.clip(np.searchsorted(table, a, side="left"), 0, 0x7E)
+    lo = np.clip(hi - 1, 0, 0x7E)
+    d_lo = a - table[lo]
+    d_hi = table[hi] - a
+    take_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(take_hi, hi, lo).astype(np.uint8)
+    code = code | (np.signbit(x).astype(np.uint8) << np.uint8(7))
+    return np.where(np.isnan(x), np.uint8(0x7F), code).astype(np.uint8)
