@@ -59,6 +59,9 @@ def parse():
     ap.add_argument("--schedule", default="balanced", choices=["balanced", "tile"],
                     help="attention schedule: balanced shares of (query tile x key tile) steps with a "
                          "merge of split tiles (needs a workspace), or one workgroup per query tile")
+    ap.add_argument("--quantize-append", action="store_true",
+                    help="fp8round: new K/V arrive as bf16 and the append quantises them to E4M3FN "
+                         "(wf_kv_append_quantize) instead of copying pre-quantised pages")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the timed run, copy a buffer of this many MiB once (a plain copy kernel of "
                          "known size that scales the FETCH_SIZE / WRITE_SIZE counters of a profiled run)")
@@ -99,7 +102,7 @@ def pct(xs, q):
 class Layer:
     """One layer's cache plus the device inputs of its chunk."""
 
-    def __init__(self, wf, torch, synth, cfg, layer, gen):
+    def __init__(self, wf, torch, synth, cfg, layer, gen, bf16_source=False):
         H, D, dt = cfg["H"], cfg["D"], cfg["dtype"]
         n = cfg.get("chunk", CHUNK)
         table = synth.permuted_table(synth.W_WAN_ROUND if dt == "bf16" else synth.W_14B_FP8, layer, 21)
@@ -107,7 +110,7 @@ class Layer:
         std = cfg["std"]
         self.q = (torch.randn((n, H, D), generator=gen, device="cuda") * std).to(torch.bfloat16)
         self.o = torch.empty_like(self.q)
-        if dt == "bf16":
+        if dt == "bf16" or bf16_source:
             self.k = (torch.randn((n, H, D), generator=gen, device="cuda") * std).to(torch.bfloat16)
             self.v = (torch.randn((n, H, D), generator=gen, device="cuda") * std).to(torch.bfloat16)
             self.ks = self.vs = None
@@ -144,13 +147,20 @@ def run_round(args, cfg):
     wf.lib()
     gen = torch.Generator(device="cuda")
     gen.manual_seed(synth.SEED)
-    layers = [Layer(wf, torch, synth, cfg, l, gen) for l in range(cfg["layers"])]
+    quant = cfg["dtype"] == "fp8" and getattr(args, "quantize_append", False)
+    layers = [Layer(wf, torch, synth, cfg, l, gen, bf16_source=quant) for l in range(cfg["layers"])]
+
+    def append(L, pos):
+        if quant:
+            wf.wf_kv_append_quantize(L.cache, pos, L.k, L.v)
+        else:
+            wf.wf_kv_append(L.cache, pos, L.k, L.v, L.ks, L.vs)
     H, D = cfg["H"], cfg["D"]
     n = cfg.get("chunk", CHUNK)
     # prefill 18 frames per layer with the layer's chunk data
     for L in layers:
         for c in range(18 * FRAME // n):
-            wf.wf_kv_append(L.cache, c * n, L.k, L.v, L.ks, L.vs)
+            append(L, c * n)
     torch.cuda.synchronize()
     ev = lambda: torch.cuda.Event(enable_timing=True)
     ws = wf.workspace_for(layers[0].cache, "cuda") if args.schedule == "balanced" else None
@@ -164,7 +174,7 @@ def run_round(args, cfg):
             e0 = ev() if record else None
             if record:
                 e0.record()
-            wf.wf_kv_append(c, c.end, L.k, L.v, L.ks, L.vs)
+            append(L, c.end)
             e1 = ev() if record else None
             if record:
                 e1.record()
@@ -199,6 +209,8 @@ def run_round(args, cfg):
     app_bytes = 2 * 2 * n * H * D * esize
     if cfg["dtype"] == "fp8":
         app_bytes += 2 * 2 * (n // FRAME) * H * (-(-FRAME // 128)) * 4
+    if quant:  # read bf16, write e4m3 codes and the scales
+        app_bytes = 2 * n * H * D * (2 + 1) + 2 * (n // FRAME) * H * (-(-FRAME // 128)) * 4
     total_flops = flops_per_launch * len(att_ms)
     ms_step = total_ms / args.steps
     avg_att = sum(att_ms) / len(att_ms)
@@ -317,6 +329,8 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if cfg["dtype"] == "bf16" else "e4m3 (fp8 MFMA; bf16 Q and P quantised in-kernel, e4m3 K,V)",
+        "append_mode": ("quantising bf16 -> e4m3" if getattr(args, "quantize_append", False) and cfg["dtype"] == "fp8"
+                        else "copy"),
         "data": "synthetic (seeded N(0, s^2) on device, random page tables)",
         "config": {"workload": cfg["name"], "layers": cfg["layers"], "heads": r["H"], "head_dim": r["D"],
                    "query_rows": cfg.get("chunk", CHUNK), "keys": WINDOW if "round" in args.workload else None,
@@ -337,8 +351,10 @@ def main():
         out["append_kernel_ms_p10_p50_p90"] = [round(pct(app, q), 5) for q in (0.1, 0.5, 0.9)]
         out["append_roofline"] = {"bound": "hbm", "achieved": round(r["append_gbps"], 1), "peak": HBM_PEAK_GBPS,
                                   "unit": "GB/s", "frac": round(r["append_gbps"] / HBM_PEAK_GBPS, 4),
-                                  "traffic": hbm_traffic("append_kernel", args.workload, "kv_cache.hip"),
-                                  "kernel": "append_kernel<%d, 128>" % (2 if cfg["dtype"] == "bf16" else 1),
+                                  "traffic": (hbm_traffic("append_kernel", args.workload, "kv_cache.hip")
+                                              if out["append_mode"] == "copy" else None),
+                                  "kernel": ("quant_append_kernel<128>" if out["append_mode"] != "copy" else
+                                             "append_kernel<%d, 128>" % (2 if cfg["dtype"] == "bf16" else 1)),
                                   "bytes_per_launch": r["append_bytes"]}
     if args.calib_copy_mib > 0:
         calib_copy(args.calib_copy_mib)

@@ -66,11 +66,12 @@ def lib():
         L.wf_kv_cache_bytes.argtypes = [P, ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(ctypes.c_uint64)]
         L.wf_kv_append.argtypes = [P, i64, i32, vp, vp, vp, vp, vp]
         L.wf_kv_evict.argtypes = [P, i32, ctypes.c_uint32, vp]
+        L.wf_kv_append_quantize.argtypes = [P, i64, i32, vp, vp, vp]
         L.wf_chunk_attn_fwd.argtypes = [P, vp, i32, vp, vp, i32, ctypes.POINTER(i32), ctypes.POINTER(i64),
                                         ctypes.POINTER(i64), f32, vp, ctypes.c_uint64, vp]
         L.wf_chunk_attn_workspace_bytes.argtypes = [P, ctypes.POINTER(ctypes.c_uint64)]
         for name in ("wf_kv_cache_check", "wf_kv_cache_bytes", "wf_kv_append", "wf_kv_evict", "wf_chunk_attn_fwd",
-                     "wf_chunk_attn_workspace_bytes"):
+                     "wf_chunk_attn_workspace_bytes", "wf_kv_append_quantize"):
             getattr(L, name).restype = ctypes.c_int
         L.wf_last_error.restype = ctypes.c_char_p
         L.wf_last_error.argtypes = []
@@ -154,6 +155,13 @@ def wf_kv_append(cache, pos, k_new, v_new, k_scale_new=None, v_scale_new=None, s
     n = int(k_new.shape[0])
     _check(lib().wf_kv_append(ctypes.byref(cache.c), int(pos), n, _ptr(k_new), _ptr(v_new),
                               _ptr(k_scale_new), _ptr(v_scale_new), _stream(stream)))
+
+
+def wf_kv_append_quantize(cache, pos, k_new, v_new, stream=None):
+    """Quantise bf16 rows k_new/v_new [n, H, D] to E4M3FN (per page, head, 128-token block) and append."""
+    n = int(k_new.shape[0])
+    _check(lib().wf_kv_append_quantize(ctypes.byref(cache.c), int(pos), n, _ptr(k_new), _ptr(v_new),
+                                       _stream(stream)))
 
 
 def wf_kv_evict(cache, n, poison=False, stream=None):

@@ -204,6 +204,56 @@ wf_status wf_kv_append(wf_kv_cache* c, int64_t pos, int32_t n, const void* k_new
   return ok();
 }
 
+wf_status wf_kv_append_quantize(wf_kv_cache* c, int64_t pos, int32_t n, const void* k_new, const void* v_new,
+                                void* stream) {
+  wf_status s = check_layout(c);
+  if (s != WF_OK) return s;
+  if ((s = check_window(c)) != WF_OK) return s;
+  if (c->kv_dtype != WF_FP8_E4M3) return fail(WF_ERR_UNSUPPORTED, "wf_kv_append_quantize needs an E4M3FN cache");
+  if (n < 0) return fail(WF_ERR_INVALID_ARG, "n = %d is negative", n);
+  if (pos < c->start || pos > c->end)
+    return fail(WF_ERR_RANGE, "append position %lld outside [start %lld, end %lld]", (long long)pos,
+                (long long)c->start, (long long)c->end);
+  const int64_t cap = (int64_t)c->table_len * c->page_size;
+  if (pos + n > c->start + cap)
+    return fail(WF_ERR_CAPACITY, "append [%lld, %lld) overruns live tokens (start %lld, capacity %lld)",
+                (long long)pos, (long long)(pos + n), (long long)c->start, (long long)cap);
+  if (pos % c->page_size != 0 || n % c->page_size != 0)
+    return fail(WF_ERR_INVALID_ARG, "quantising appends must be whole pages (pos %lld, n %d, page %d)",
+                (long long)pos, n, c->page_size);
+  if (n == 0) return ok();
+  if (k_new == nullptr || v_new == nullptr) return fail(WF_ERR_INVALID_ARG, "k_new/v_new is NULL");
+  if (!aligned(k_new, 16) || !aligned(v_new, 16))
+    return fail(WF_ERR_INVALID_ARG, "k_new/v_new must be 16-byte aligned");
+  const uint64_t nb = (uint64_t)n * c->num_heads * c->head_dim * 2;
+  const uint64_t kvb = kv_bytes_of(c);
+  if (overlap(k_new, nb, c->k, kvb) || overlap(k_new, nb, c->v, kvb) || overlap(v_new, nb, c->k, kvb) ||
+      overlap(v_new, nb, c->v, kvb))
+    return fail(WF_ERR_INVALID_ARG, "new K/V overlap the cache buffers");
+  wf::QuantAppendParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.k_new = k_new;
+  p.v_new = v_new;
+  p.k = c->k;
+  p.v = c->v;
+  p.ks = c->k_scale;
+  p.vs = c->v_scale;
+  p.npages = n / c->page_size;
+  p.H = c->num_heads;
+  p.D = c->head_dim;
+  p.P = c->page_size;
+  p.T = c->table_len;
+  p.nblk = (c->page_size + WF_SCALE_BLOCK - 1) / WF_SCALE_BLOCK;
+  p.base_slot = (int32_t)((pos / c->page_size) % c->table_len);
+  std::memcpy(p.table, c->page_table, sizeof(int32_t) * c->table_len);
+  if ((int64_t)p.npages * p.nblk >= ((int64_t)1 << 31))
+    return fail(WF_ERR_UNSUPPORTED, "append of %d tokens needs too many blocks", n);
+  hipError_t e = wf::launch_quant_append(p, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(WF_ERR_HIP, "quantising append launch failed: %s", hipGetErrorString(e));
+  c->end = std::max(c->end, pos + n);
+  return ok();
+}
+
 wf_status wf_kv_evict(wf_kv_cache* c, int32_t n, uint32_t flags, void* stream) {
   wf_status s = check_layout(c);
   if (s != WF_OK) return s;

@@ -167,6 +167,113 @@ __global__ __launch_bounds__(kThreads) void append_kernel(const AppendParams p) 
   }
 }
 
+// Quantising append.  One block = one 128-token scale block of one new page
+// and one head.  K and V rows (bf16) are read once into registers:
+//   amax = max |x| over the block (fp32, exact), scale = amax / 448 and
+//   r = 448 / amax (correctly rounded divisions; 1, 1 for an all-zero block),
+//   code = e4m3(x * r): fp32 multiply, then v_cvt_pk_fp8_f32 (round to
+//   nearest even, saturating at 448).
+// K codes go straight to the page rows; V codes are transposed through LDS
+// into the page's V^T rows.
+constexpr int kQBlock = WF_SCALE_BLOCK;  // tokens per scale block
+
+__device__ __forceinline__ float block_max(float x, float* red) {
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  float m = red[0];
+#pragma unroll
+  for (int w = 1; w < kThreads / 64; ++w) m = fmaxf(m, red[w]);
+  return m;
+}
+
+// 8 bf16 values times r -> 8 e4m3 codes (one 64-bit word).
+__device__ __forceinline__ uint2 quant8(uint4 raw, float r) {
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+  uint32_t out[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const float a0 = __uint_as_float(w[2 * h] << 16) * r, a1 = __uint_as_float(w[2 * h] & 0xFFFF0000u) * r;
+    const float a2 = __uint_as_float(w[2 * h + 1] << 16) * r, a3 = __uint_as_float(w[2 * h + 1] & 0xFFFF0000u) * r;
+    uint32_t v = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a0, a1, 0, false);
+    out[h] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a2, a3, (int)v, true);
+  }
+  return make_uint2(out[0], out[1]);
+}
+
+__device__ __forceinline__ float absmax8(uint4 raw) {
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    m = fmaxf(m, fmaxf(fabsf(__uint_as_float(w[i] << 16)), fabsf(__uint_as_float(w[i] & 0xFFFF0000u))));
+  return m;
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void quant_append_kernel(const QuantAppendParams p) {
+  constexpr int CH = D / 8;                  // 8-element chunks per row
+  constexpr int NR = kQBlock * CH / kThreads;  // chunks per thread
+  constexpr int VSTRIDE = kQBlock + 8;       // LDS bytes per V^T row (8-byte aligned rows)
+  __shared__ float red[kThreads / 64];
+  __shared__ __align__(16) uint8_t vt[D * VSTRIDE];
+  const int tid = threadIdx.x;
+  const int h = blockIdx.y;
+  const int j = blockIdx.x / p.nblk;          // new page
+  const int b = blockIdx.x - j * p.nblk;      // scale block inside the page
+  const int t0 = kQBlock * b;
+  const int nt = min(kQBlock, p.P - t0);      // tokens in this block
+  int slot = p.base_slot + j;
+  slot -= (slot / p.T) * p.T;
+  const int64_t ph = (int64_t)p.table[slot] * p.H + h;
+  const int64_t row0 = (int64_t)j * p.P + t0;  // first new row of the block
+  const uint32_t src_stride = (uint32_t)p.H * D * 2;
+  const char* ksrc = (const char*)p.k_new + (row0 * p.H + h) * D * 2;
+  const char* vsrc = (const char*)p.v_new + (row0 * p.H + h) * D * 2;
+
+  uint4 kr[NR], vr[NR];
+  float km = 0.f, vm = 0.f;
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const int idx = tid + kThreads * r, t = idx / CH, c = idx % CH;
+    kr[r] = vr[r] = make_uint4(0u, 0u, 0u, 0u);
+    if (t < nt) {
+      kr[r] = *(const uint4*)(ksrc + (uint32_t)t * src_stride + c * 16);
+      vr[r] = *(const uint4*)(vsrc + (uint32_t)t * src_stride + c * 16);
+    }
+    km = fmaxf(km, absmax8(kr[r]));
+    vm = fmaxf(vm, absmax8(vr[r]));
+  }
+  km = block_max(km, red);
+  __syncthreads();
+  vm = block_max(vm, red);
+  const float kscale = km > 0.f ? __fdiv_rn(km, 448.f) : 1.f, kr_ = km > 0.f ? __fdiv_rn(448.f, km) : 1.f;
+  const float vscale = vm > 0.f ? __fdiv_rn(vm, 448.f) : 1.f, vr_ = vm > 0.f ? __fdiv_rn(448.f, vm) : 1.f;
+  if (tid == 0) {
+    p.ks[ph * p.nblk + b] = kscale;
+    p.vs[ph * p.nblk + b] = vscale;
+  }
+  char* kdst = (char*)p.k + (ph * p.P + t0) * D;
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const int idx = tid + kThreads * r, t = idx / CH, c = idx % CH;
+    const uint2 kq = quant8(kr[r], kr_);
+    const uint2 vq = quant8(vr[r], vr_);
+    if (t < nt) *(uint2*)(kdst + (uint32_t)t * D + c * 8) = kq;
+    const uint8_t* vb = (const uint8_t*)&vq;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) vt[(c * 8 + e) * VSTRIDE + t] = vb[e];
+  }
+  __syncthreads();
+  // V^T rows: for each dim d, nt consecutive bytes at page offset t0.
+  char* vdst = (char*)p.v + ph * (int64_t)D * p.P + t0;
+  const int words = (nt + 7) / 8;  // 8-byte words per row (nt is a multiple of 8)
+  for (int idx = tid; idx < D * words; idx += kThreads) {
+    const int d = idx / words, w = idx - d * words;
+    *(uint2*)(vdst + (int64_t)d * p.P + 8 * w) = *(const uint2*)(vt + d * VSTRIDE + 8 * w);
+  }
+}
+
 // Overwrite evicted rows with NaN codes (test aid).  Block = one token, all heads.
 template <int ESIZE>
 __global__ __launch_bounds__(kThreads) void poison_kernel(const PoisonParams p) {
@@ -204,6 +311,15 @@ hipError_t launch_append_e(const AppendParams& p, int ntiles, hipStream_t s) {
 }
 
 }  // namespace
+
+hipError_t launch_quant_append(const QuantAppendParams& p, hipStream_t s) {
+  const dim3 grid(p.npages * p.nblk, p.H);
+  if (p.D == 128)
+    hipLaunchKernelGGL(quant_append_kernel<128>, grid, dim3(kThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL(quant_append_kernel<64>, grid, dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
 
 hipError_t launch_append(const AppendParams& p, int ntiles, hipStream_t s) {
   switch (p.esize) {

@@ -78,6 +78,21 @@ struct PoisonParams {
 };
 
 hipError_t launch_append(const AppendParams& p, int ntiles, hipStream_t s);
+
+// Quantising append: bf16 rows -> E4M3FN codes + per-(page, head, block) scales.
+struct QuantAppendParams {
+  const void* k_new;      // bf16 [n][H][D]
+  const void* v_new;
+  void* k;                // E4M3FN pages [pages][H][P][D]
+  void* v;                // [pages][H][D][P]
+  float* ks;              // [pages][H][nblk]
+  float* vs;
+  int32_t npages;         // new pages (n / P)
+  int32_t H, D, P, T, nblk;
+  int32_t base_slot;      // ring slot of the first new page
+  int32_t table[WF_MAX_TABLE_LEN];
+};
+hipError_t launch_quant_append(const QuantAppendParams& p, hipStream_t s);
 hipError_t launch_poison(const PoisonParams& p, hipStream_t s);
 
 // ---------------------------------------------------------------- attention

@@ -130,6 +130,24 @@ wf_status wf_kv_append(wf_kv_cache *cache, int64_t pos, int32_t n, const void *k
                        void *stream);
 
 /*
+ * Quantise bf16 rows to E4M3FN and append them to an E4M3FN cache: the
+ * producer side of a cache held in fp8 (the pages' quantised attention
+ * backends; scope-causal-forcing README, "How It Works", step 2 writes the
+ * cache).  For each new page, head and 128-token scale block:
+ *     amax  = max |x| over the block's tokens and dims (float32),
+ *     scale = amax / 448,  r = 448 / amax  (float32 divisions rounded to
+ *             nearest; 1 and 1 for an all-zero block),
+ *     code  = E4M3FN(x * r)  (float32 product rounded to nearest, converted
+ *             with round-to-nearest-even, saturating at +-448).
+ *   k_new, v_new   device bf16 [n][num_heads][head_dim] token-major, finite.
+ * Requires kv_dtype == WF_FP8_E4M3, pos and n multiples of page_size, and the
+ * position rules of wf_kv_append.  On success end = max(end, pos + n).  Codes
+ * and scales are bit-exact with the definition above.
+ */
+wf_status wf_kv_append_quantize(wf_kv_cache *cache, int64_t pos, int32_t n, const void *k_new,
+                                const void *v_new, void *stream);
+
+/*
  * Drop the n oldest live tokens: start += n (rolling window).  Requires
  * 0 <= n <= end - start.  No kernel is launched unless flags has
  * WF_EVICT_POISON, which overwrites the evicted rows with NaN codes so that a

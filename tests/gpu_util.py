@@ -68,6 +68,10 @@ class Pair:
         wf.wf_kv_append(self.gpu, pos, dev(k, d), dev(v, d), dev(ks, "scale"), dev(vs, "scale"))
         self.ref.append(pos, k, v, ks, vs)
 
+    def append_quantize(self, pos, k_bf16, v_bf16):
+        wf.wf_kv_append_quantize(self.gpu, pos, dev(k_bf16, "bf16"), dev(v_bf16, "bf16"))
+        self.ref.append_quantized(pos, k_bf16, v_bf16)
+
     def evict(self, n, poison=False):
         wf.wf_kv_evict(self.gpu, n, poison=poison)
         self.ref.evict(n, poison=poison)

@@ -88,3 +88,45 @@ def test_evict_poison_bitexact(dtype):
     pair.append(0, k, k, ks, ks)
     pair.evict(P + 5, poison=True)
     assert pair.pages_equal()
+
+
+@pytest.mark.parametrize("P,D", [(64, 128), (200, 64), (1560, 128)])
+def test_quantizing_append_bitexact(P, D):
+    """bf16 rows -> E4M3FN codes + per-(page, head, block) scales, byte-exact with the oracle's
+    quantiser over several rounds (overwrite, evict, ring wrap), including all-zero and tiny blocks."""
+    print("case: quantizing append P%d D%d" % (P, D), flush=True)
+    H, T = 3, 5
+    rng = np.random.default_rng(P + D)
+    pair = Pair(T + 2, P, H, D, "fp8", list(rng.permutation(T + 2)[:T]), fill_seed=9)
+    pos = 0
+    for r in range(7):
+        n = P * (1 + r % 2)
+        if pair.gpu.end - pair.gpu.start + n > pair.gpu.capacity:
+            pair.evict(pair.gpu.end - pair.gpu.start + n - pair.gpu.capacity)
+        x = rng.standard_normal((2, n, H, D)).astype(np.float32) * rng.choice([1.0, 30.0, 1e-3])
+        x[:, : min(n, 128), r % H] = 0.0                      # an all-zero block
+        x[1, -8:, (r + 1) % H] *= 1e-6                        # tiny values (code rounding to zero)
+        k, v = synth.bf16_codes(x[0]), synth.bf16_codes(x[1])
+        if r == 4:
+            pos = pair.gpu.end - n                            # rewrite the newest pages
+        else:
+            pos = pair.gpu.end
+        pair.append_quantize(pos, k, v)
+        assert pair.pages_equal(), "round %d" % r
+
+
+def test_attention_over_quantized_cache():
+    """The fp8 attention kernel over pages written by the quantising append, vs the oracle."""
+    from gpu_util import dev, errors, host_values, values_of
+    print("case: attention over quantized cache", flush=True)
+    H, D, P = 4, 128, 256
+    rng = np.random.default_rng(12)
+    pair = Pair(12, P, H, D, "fp8", list(rng.permutation(12)))
+    x = rng.standard_normal((2, 10 * P, H, D)).astype(np.float32)
+    pair.append_quantize(0, synth.bf16_codes(x[0]), synth.bf16_codes(x[1]))
+    q = synth.bf16_codes(rng.standard_normal((300, H, D)).astype(np.float32))
+    o, lse = pair.attend(dev(q, "bf16"), [0, 100, 300], [5, 0], [2560, 1999])
+    ro, rl = pair.reference(values_of(q, "bf16"), [0, 100, 300], [5, 0], [2560, 1999])
+    mx, mean, rel = errors(host_values(o), ro)
+    print("max-abs %.3e rel-L2 %.3e" % (mx, rel), flush=True)
+    assert mx <= 5e-2 and rel <= 6e-2
