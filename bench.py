@@ -62,6 +62,9 @@ def parse():
     ap.add_argument("--quantize-append", action="store_true",
                     help="fp8round: new K/V arrive as bf16 and the append quantises them to E4M3FN "
                          "(wf_kv_append_quantize) instead of copying pre-quantised pages")
+    ap.add_argument("--graph", action="store_true",
+                    help="round workloads: after the eager run, replay the round from captured HIP graphs "
+                         "(one per ring phase) for the same number of steps and report its rate")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the timed run, copy a buffer of this many MiB once (a plain copy kernel of "
                          "known size that scales the FETCH_SIZE / WRITE_SIZE counters of a profiled run)")
@@ -215,7 +218,27 @@ def run_round(args, cfg):
     ms_step = total_ms / args.steps
     avg_att = sum(att_ms) / len(att_ms)
     avg_app = sum(app_ms) / len(app_ms)
+    graph = None
+    if getattr(args, "graph", False) and not quant:
+        from chunk_causal_dit_wf_amd.round import Layer as RLayer, StreamingRound
+        rr = StreamingRound([RLayer(L.cache, L.q, L.k, L.v, L.o, L.ks, L.vs) for L in layers], n, WINDOW,
+                            workspace=ws)
+        rr.capture()
+        for _ in range(rr.period):
+            rr.replay()
+        torch.cuda.synchronize()
+        g0, g1 = ev(), ev()
+        g0.record()
+        for _ in range(args.steps):
+            rr.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        gms = g0.elapsed_time(g1) / args.steps
+        graph = dict(graph_ms_per_step=round(gms, 4), graph_chunks_per_s=round(1000.0 / gms, 3),
+                     graph_tflops=round(flops_per_launch * cfg["layers"] / (gms * 1e-3) / 1e12, 2),
+                     graph_phases=rr.period)
     return dict(
+        graph=graph,
         ms_per_step=ms_step, wall_s=wall, value=total_flops / (total_ms * 1e-3) / 1e12,
         attn_kernel_ms=avg_att, attn_tflops=flops_per_launch / (avg_att * 1e-3) / 1e12, att_ms=att_ms,
         append_kernel_ms=avg_app, append_gbps=app_bytes / (avg_app * 1e-3) / 1e9, app_ms=app_ms,
@@ -356,6 +379,8 @@ def main():
                                   "kernel": ("quant_append_kernel<128>" if out["append_mode"] != "copy" else
                                              "append_kernel<%d, 128>" % (2 if cfg["dtype"] == "bf16" else 1)),
                                   "bytes_per_launch": r["append_bytes"]}
+    if r.get("graph"):
+        out["graph_replay"] = r["graph"]
     if args.calib_copy_mib > 0:
         calib_copy(args.calib_copy_mib)
     if not args.no_cpu_baseline:
