@@ -206,3 +206,20 @@ int main() {
     assert r.returncode == 0, r.stderr[-2000:]
     out = subprocess.run([str(exe)], capture_output=True, text=True)
     assert out.returncode == 0 and out.stdout.strip() == "0"
+
+
+def test_quantizing_append_validation():
+    k = torch.zeros(64, 2, 64, dtype=torch.bfloat16)
+    b = _cache("bf16")
+    assert _status(wf.wf_kv_append_quantize, b, 0, k, k) == wf.WF_ERR_UNSUPPORTED   # not an E4M3FN cache
+    f = _cache("fp8")
+    assert _status(wf.wf_kv_append_quantize, f, 8, k, k) == wf.WF_ERR_RANGE         # beyond end
+    assert _status(wf.wf_kv_append_quantize, f, 0, k[:40], k[:40]) == wf.WF_ERR_INVALID_ARG  # not whole pages
+    raw = torch.zeros(64 * 2 * 64 + 8, dtype=torch.bfloat16)
+    mis = raw[1:1 + 64 * 2 * 64].view(64, 2, 64)
+    assert _status(wf.wf_kv_append_quantize, f, 0, mis, k) == wf.WF_ERR_INVALID_ARG  # misaligned source
+    assert _status(wf.wf_kv_append_quantize, f, 0, k[:0], k[:0]) == wf.WF_OK         # nothing to do
+    assert (f.start, f.end) == (0, 0)
+    if not torch.cuda.is_available():
+        assert _status(wf.wf_kv_append_quantize, f, 0, k, k) == wf.WF_ERR_HIP
+        assert (f.start, f.end) == (0, 0)
