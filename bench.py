@@ -74,7 +74,7 @@ def parse():
 def kernel_of(dtype):
     """Attention kernel the library launches for a workload (the dispatch rule of wf_chunk_attn_fwd:
     caches with pages of >= 64 tokens take the LDS-DMA kernels, bf16 or fp8 MFMA)."""
-    return "attn_fwd_dma_kernel<128>" if dtype == "bf16" else "attn_fwd_fp8_kernel<128>"
+    return "attn_fwd_pp_kernel<128>" if dtype == "bf16" else "attn_fwd_fp8_kernel<128>"
 
 
 def source_sha(name):

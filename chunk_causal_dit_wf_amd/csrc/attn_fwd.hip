@@ -455,45 +455,52 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(const AttnParams p
 }  // namespace staged
 
 // ---------------------------------------------------------------------------
-// bf16 kernel with LDS-DMA tile loads (bf16 cache, pages >= 64 tokens,
-// cache < 4 GiB).
+// bf16 kernel with LDS-DMA tile loads (bf16 cache, pages >= 64 tokens, cache
+// < 4 GiB), two-group ping-pong schedule.
 //
 // One workgroup = 8 waves (2 per SIMD) = 256 query rows of one head of one
-// chunk; each wave owns 32 rows and keeps its Q^T fragments in VGPRs.  The 8
-// waves share every K/V tile.
+// chunk; each wave owns 32 rows and keeps its Q^T fragments in VGPRs.  Waves
+// 0-3 (group 0) and 4-7 (group 1) put one wave on each SIMD (waves w and w+4
+// share one), and the two groups run the same program one phase apart: while
+// one wave of a SIMD issues the matrix products of a 64-key tile (phase M),
+// the other computes the softmax of its next tile on the vector unit (phase
+// V).  Every phase ends with a workgroup barrier, so the offset never drifts
+// and the matrix unit of each SIMD always has one wave feeding it.
 //
-// Tiles reach LDS through global_load_lds_dwordx4 (16 bytes per lane, written
-// to LDS at base + 16 * lane), so no VGPRs stage them.  Rows are padded by 16
-// bytes (K: 2D+16 bytes, V^T: 144 bytes) so that the 16 lanes one LDS cycle
-// serves hit distinct banks and every fragment read is an immediate offset
-// from one per-lane base; DMA lanes that land on padding load a dummy chunk.
-//   K half-tile [32 rows][D] bf16: LDS row r holds key pi(r) of the half-tile,
+// Per 64-key tile t and wave:
+//   M(t): S(t+1) = K(t+1) Q^T (two 32-key halves, 16 MFMAs) and
+//         O^T += V(t)^T P(t) (16 MFMAs); fragment reads run ahead in LDS.
+//   V(t): issue this wave's share of the tile loads, then row maxima of
+//         S(t+1), the lazy exact rescale, P(t+1) = exp2(S - m) in bf16 and
+//         row sums.
+//
+// LDS layout.  Rows are padded by 16 bytes (K: 2D+16 bytes, V^T: 144 bytes)
+// so that the lanes one LDS cycle serves hit distinct banks and every
+// fragment read is an immediate offset from one per-lane base.
+//   K half-tile [32 rows][D] bf16: LDS row r holds key pi(r) of the half,
 //     pi(8 j + 4 h + i) = 16 h + 4 j + i.  The MFMA A operand of lane l is
 //     LDS row l % 32, so in the S^T accumulator lane-half h holds the 16
-//     consecutive keys 16 h .. 16 h + 15 of the half-tile.
+//     consecutive keys 16 h .. 16 h + 15 of the half.
 //   V^T tile [D][64 keys] bf16, keys in natural order.  Because of pi the 8
-//     keys one P^T operand slot group needs are contiguous: one 16-byte LDS
-//     read per MFMA, and V^T rows are plain 16-byte DMA chunks.
-//
-// Pipeline.  The key range is walked in 32-key half-steps q; one barrier per
-// 64-key tile j (half-steps 2j, 2j+1).  Entering half-step q the wave holds
-// S[q] (masked) and a reference maximum m within 2^8 of S[q]'s row maxima,
-// with O and l relative to m:
-//   [A] S[q+1] = K[q+1] Q^T (MFMA)  ||  P[q] = exp2(S[q] - m), row sums
-//   [B] O^T += V^T[q] P^T[q] (MFMA) ||  mask S[q+1], row max of S[q+1]
-//   [C] rare exact rescale when a row max of S[q+1] exceeds m by more than 8
-// At the start of tile j the DMA for K half-tiles 2j+3, 2j+4 (ring of four)
-// and V tile j+1 (double buffer) is issued into buffers the previous tile
-// freed; V tile j's keys outside the chunk's range are zeroed first if it is
-// an edge tile (0 * NaN would poison P V); the tile ends with a wait for its
-// DMA and a barrier.
+//     keys one P^T operand needs are contiguous: one 16-byte LDS read per
+//     MFMA, and V^T rows are plain 16-byte DMA chunks.
+// Tiles stream through a ring of three LDS stages; stage t (slot (t+1) % 3)
+// holds K(t+1) and V(t)^T.  Loads are buffer LDS-DMA (16 bytes per lane,
+// written to LDS at base + 16 * lane; padding lanes load a dummy chunk).
+// Group 1 loads K tiles four tiles ahead, group 0 V^T tiles two tiles ahead,
+// at the start of their V phases, so the loads' latency is covered before
+// the wave reads LDS again.  A stage is complete once every wave has waited
+// for its own loads into it and passed a barrier.  V tiles with keys outside
+// the chunk's range (0 * NaN would poison P V) are zeroed in LDS behind one
+// extra barrier.
 // ---------------------------------------------------------------------------
-namespace dma {
+namespace pp {
 
-constexpr int NW = 8;         // waves per workgroup
-constexpr int NTD = 64 * NW;  // threads per workgroup
-constexpr int BMD = 32 * NW;  // query rows per workgroup
-constexpr int HK = 32;        // keys per K half-tile
+constexpr int NW = 8;          // waves per workgroup
+constexpr int NTD = 64 * NW;   // threads per workgroup
+constexpr int NG = 4;          // waves per group (one per SIMD)
+constexpr int BMD = 32 * NW;   // query rows per workgroup
+constexpr int HK = 32;         // keys per K half-tile
 static_assert(BMD == kBlockMDma, "host and kernel disagree on the DMA kernel block size");
 
 template <int D>
@@ -501,100 +508,158 @@ struct Geo {
   static constexpr int KROW = 2 * D + 16;                 // LDS bytes per K row (padded)
   static constexpr int KCH = D / 8;                       // 16-byte data chunks per K row
   static constexpr int KDMA = (HK * KROW + 1023) / 1024;  // DMA instructions per K half-tile
-  static constexpr int KHALF = KDMA * 1024;               // LDS bytes per K half-tile buffer
+  static constexpr int KHALF = KDMA * 1024;               // LDS bytes per K half-tile
+  static constexpr int KTILE = 2 * KHALF;                 // LDS bytes per K tile
+  static constexpr int KN = 2 * KDMA;                     // DMA instructions per K tile
   static constexpr int VROW = 2 * BN + 16;                // LDS bytes per V^T row (padded)
   static constexpr int VDMA = (D * VROW + 1023) / 1024;   // DMA instructions per V^T tile
-  static constexpr int VTILE = VDMA * 1024;               // LDS bytes per V^T tile buffer
-  static constexpr int KPW = (KDMA + NW - 1) / NW;        // max K instructions per wave
-  static constexpr int VPW = (VDMA + NW - 1) / NW;        // max V instructions per wave
+  static constexpr int VTILE = VDMA * 1024;               // LDS bytes per V^T tile
+  static constexpr int KPW = (KN + NG - 1) / NG;          // K instructions per group-1 wave (max)
+  static constexpr int VPW = (VDMA + NG - 1) / NG;        // V instructions per group-0 wave (max)
+  static constexpr int PW = KPW > VPW ? KPW : VPW;  // DMA instructions per wave and tile
 };
 
-// Per-lane constants of this wave's DMA instructions: source byte offset
-// relative to the run geometry base and the run-relative key of the 16-byte
-// chunk (for the page-break select).  Wave w issues instructions w, w + NW, ...
-// of each K half-tile and V^T tile.  Lanes that land on row padding (or past
-// the last row) load the run's first chunk, a valid address, into the slack.
+// Every wave issues exactly PW DMA instructions per tile: wave gw of a group
+// takes instructions gw, gw + 4, ... of the tile, and repeats its first one
+// (same source, same destination, same bytes) where it runs out.  The fixed
+// count lets every wait for a tile be a compile-time vmcnt.
 template <int D>
-struct DmaPlan {
-  uint32_t koff[Geo<D>::KPW];
-  int32_t kkey[Geo<D>::KPW];
-  uint32_t voff[Geo<D>::VPW];
-  int32_t vkey[Geo<D>::VPW];
+__device__ __forceinline__ int inst_of(int group, int gw, int r) {
+  const int n = gw + NG * r;
+  return n < (group == 1 ? Geo<D>::KN : Geo<D>::VDMA) ? n : gw;
+}
+
+// Per-lane source byte offsets of this wave's DMA instructions, relative to
+// the tile's first key in its page.  Padding lanes load the tile's first
+// chunk.  The tile-relative key of a lane's chunk (needed only when a tile
+// crosses a page) is recomputed from the lane instead of being kept.
+template <int D>
+struct Plan {
+  uint32_t off[Geo<D>::PW];
 };
 
+// K instruction n, lane: tile-relative key of the lane's 16-byte chunk and
+// its byte offset (row pi(key) of half n / KDMA, 16-byte chunk pc).
 template <int D>
-__device__ __forceinline__ DmaPlan<D> make_plan(int wave, int lane, int P) {
+__device__ __forceinline__ void k_chunk(int n, int lane, int& key, uint32_t& off) {
   using G = Geo<D>;
-  DmaPlan<D> pl;
+  const int half = n / G::KDMA, rr = n - half * G::KDMA;
+  const int y = 1024 * rr + 16 * lane;
+  const int row = y / G::KROW, pc = (y % G::KROW) / 16;
+  const bool data = row < HK && pc < G::KCH;
+  const int k = HK * half + 16 * ((row >> 2) & 1) + 4 * (row >> 3) + (row & 3);  // pi(row)
+  key = data ? k : 0;
+  off = data ? (uint32_t)(k * 2 * D + pc * 16) : 0u;
+}
+
+// V^T instruction n, lane: key of the lane's chunk and its byte offset (row d
+// of the V^T block, keys 8 pc .. 8 pc + 7).
+template <int D>
+__device__ __forceinline__ void v_chunk(int n, int lane, int P, int& key, uint32_t& off) {
+  using G = Geo<D>;
+  const int y = 1024 * n + 16 * lane;
+  const int d = y / G::VROW, pc = (y % G::VROW) / 16;
+  const bool data = d < D && pc < 8;
+  key = data ? pc * 8 : 0;
+  off = data ? (uint32_t)(d * P * 2 + pc * 16) : 0u;
+}
+
+template <int D>
+__device__ __forceinline__ Plan<D> make_plan(int group, int gw, int lane, int P) {
+  Plan<D> pl;
 #pragma unroll
-  for (int r = 0; r < G::KPW; ++r) {
-    const int y = 1024 * (wave + NW * r) + 16 * lane;  // LDS byte inside the K half-tile buffer
-    const int row = y / G::KROW, pc = (y % G::KROW) / 16;
-    const bool data = row < HK && pc < G::KCH;
-    const int key = 16 * ((row >> 2) & 1) + 4 * (row >> 3) + (row & 3);  // pi(row)
-    pl.kkey[r] = data ? key : 0;
-    pl.koff[r] = data ? (uint32_t)(key * 2 * D + pc * 16) : 0u;
-  }
-#pragma unroll
-  for (int r = 0; r < G::VPW; ++r) {
-    const int y = 1024 * (wave + NW * r) + 16 * lane;  // LDS byte inside the V^T tile buffer
-    const int d = y / G::VROW, pc = (y % G::VROW) / 16;
-    const bool data = d < D && pc < 8;
-    pl.vkey[r] = data ? pc * 8 : 0;
-    pl.voff[r] = data ? (uint32_t)(d * P * 2 + pc * 16) : 0u;
+  for (int r = 0; r < Geo<D>::PW; ++r) {
+    int key;
+    if (group == 1)
+      k_chunk<D>(inst_of<D>(1, gw, r), lane, key, pl.off[r]);
+    else
+      v_chunk<D>(inst_of<D>(0, gw, r), lane, P, key, pl.off[r]);
   }
   return pl;
 }
 
-// DMA the K half-tile at cursor c (32 keys) into khalf.  Runs inside one page
-// (all but about one in P / 32) add the run's byte base to the lane's plan
-// offset; a run that crosses a page selects its page per lane.  Sources are
-// the cache base plus one 32-bit offset per lane (the scalar-base form of the
-// load).
-template <int D>
-__device__ __forceinline__ void dma_k(const AttnParams& p, const Cursor& c, const DmaPlan<D>& pl, char* khalf,
-                                      int wave) {
-  using G = Geo<D>;
-  if (p.P - c.off >= HK) {
-    const uint32_t soff = c.k0 + (uint32_t)c.off * (2 * D);
-#pragma unroll
-    for (int r = 0; r < G::KPW; ++r)
-      if ((NW - 1) + NW * r < G::KDMA || wave + NW * r < G::KDMA)
-        dma16((const char*)p.k + (soff + pl.koff[r]), khalf + 1024 * (wave + NW * r));
-    return;
-  }
-  const RunGeom g = run_geom<2 * D, 2>(p, c);
-#pragma unroll
-  for (int r = 0; r < G::KPW; ++r)
-    if (wave + NW * r < G::KDMA)
-      dma16((const char*)p.k + ((pl.kkey[r] < g.split ? g.kb0 : g.kb1) + pl.koff[r]),
-            khalf + 1024 * (wave + NW * r));
+// Buffer resource over a whole cache (K or V): raw addressing, byte offsets
+// below 2^32 (the DMA kernels take caches under 4 GiB).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t cache_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0xFFFFFFFFu, 0x00020000);
 }
 
-// DMA the V^T tile at cursor c (64 keys) into vbuf (same scheme as dma_k).
+// LDS-DMA through a buffer resource: lane L's 16 bytes at byte voff + soff of
+// the resource land at lds + 16 L.  (The buffer form keeps the compiler's
+// wait tracking exact for LDS reads issued while such loads are in flight.)
+__device__ __forceinline__ void dma16b(__amdgpu_buffer_rsrc_t rs, void* lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+}
+
+// DMA the K tile (64 keys) at cursor c into kt (group 1).
 template <int D>
-__device__ __forceinline__ void dma_v(const AttnParams& p, const Cursor& c, const DmaPlan<D>& pl, char* vbuf,
-                                      int wave) {
+__device__ __forceinline__ void dma_k(const AttnParams& p, __amdgpu_buffer_rsrc_t rs, const Cursor& c,
+                                      const Plan<D>& pl, char* kt, int gw) {
   using G = Geo<D>;
+  auto dst = [&](int r) {
+    const int n = inst_of<D>(1, gw, r);
+    const int half = n / G::KDMA;
+    return kt + half * G::KHALF + 1024 * (n - half * G::KDMA);
+  };
   if (p.P - c.off >= BN) {
-    const uint32_t soff = c.v0 + (uint32_t)c.off * 2;
+    const uint32_t soff = __builtin_amdgcn_readfirstlane(c.k0 + (uint32_t)c.off * (2 * D));  // uniform
 #pragma unroll
-    for (int r = 0; r < G::VPW; ++r)
-      if ((NW - 1) + NW * r < G::VDMA || wave + NW * r < G::VDMA)
-        dma16((const char*)p.v + (soff + pl.voff[r]), vbuf + 1024 * (wave + NW * r));
+    for (int r = 0; r < G::PW; ++r) dma16b(rs, dst(r), pl.off[r], soff);
     return;
   }
   const RunGeom g = run_geom<2 * D, 2>(p, c);
+  const int lane = __lane_id();
 #pragma unroll
-  for (int r = 0; r < G::VPW; ++r)
-    if (wave + NW * r < G::VDMA)
-      dma16((const char*)p.v + ((pl.vkey[r] < g.split ? g.vb0 : g.vb1) + pl.voff[r]),
-            vbuf + 1024 * (wave + NW * r));
+  for (int r = 0; r < G::PW; ++r) {
+    int key;
+    uint32_t off;
+    k_chunk<D>(inst_of<D>(1, gw, r), lane, key, off);
+    dma16b(rs, dst(r), (key < g.split ? g.kb0 : g.kb1) + off, 0u);
+  }
 }
 
-// Zero the keys of V^T tile t (in LDS) that lie outside [lo, hi).
+// DMA the V^T tile (64 keys) at cursor c into vt (group 0).
 template <int D>
-__device__ __forceinline__ void zero_v_outside(char* vbuf, int t, int lo, int hi) {
+__device__ __forceinline__ void dma_v(const AttnParams& p, __amdgpu_buffer_rsrc_t rs, const Cursor& c,
+                                      const Plan<D>& pl, char* vt, int gw) {
+  using G = Geo<D>;
+  auto dst = [&](int r) { return vt + 1024 * inst_of<D>(0, gw, r); };
+  if (p.P - c.off >= BN) {
+    const uint32_t soff = __builtin_amdgcn_readfirstlane(c.v0 + (uint32_t)c.off * 2);  // uniform
+#pragma unroll
+    for (int r = 0; r < G::PW; ++r) dma16b(rs, dst(r), pl.off[r], soff);
+    return;
+  }
+  const RunGeom g = run_geom<2 * D, 2>(p, c);
+  const int lane = __lane_id();
+#pragma unroll
+  for (int r = 0; r < G::PW; ++r) {
+    int key;
+    uint32_t off;
+    v_chunk<D>(inst_of<D>(0, gw, r), lane, p.P, key, off);
+    dma16b(rs, dst(r), (key < g.split ? g.vb0 : g.vb1) + off, 0u);
+  }
+}
+
+// Workgroup barrier that leaves outstanding loads in flight: the caller
+// orders the LDS data itself (each wave waits for its own DMA before the
+// barrier).  The empty asm statements keep the compiler from moving memory
+// accesses across it, the scheduling barriers keep the phases' instructions
+// on their side of it.
+__device__ __forceinline__ void barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// s_waitcnt lgkmcnt(0) alone (LDS writes done before a barrier).
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// Zero the keys of V^T tile t (in LDS) that lie outside [lo, hi) (all threads).
+template <int D>
+__device__ __forceinline__ void zero_v_outside(char* vt, int t, int lo, int hi) {
   for (int idx = threadIdx.x; idx < D * 8; idx += NTD) {
     const int d = idx >> 3, c = idx & 7;
     const int rel = t * BN + 8 * c;
@@ -602,142 +667,175 @@ __device__ __forceinline__ void zero_v_outside(char* vbuf, int t, int lo, int hi
     uint32_t m = 0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) m |= (rel + e >= lo && rel + e < hi) ? 1u << e : 0u;
-    uint4* a = (uint4*)(vbuf + d * Geo<D>::VROW + 16 * c);
+    uint4* a = (uint4*)(vt + d * Geo<D>::VROW + 16 * c);
     *a = mask_bf16x8(*a, m);
   }
 }
 
-// One 32-key half-step as explicitly ordered stages.  Stage i of [A] issues
-// the LDS read of the K fragment two stages ahead, one MFMA of the S[q+1]
-// chain (k-step i), and exponent / bf16 packing / row sum for two elements of
-// S[q].  Stage i of [B] issues the V fragment read two stages ahead, one O^T
-// MFMA (d block i % DB, P slot group i / DB), and masking + row max for two
-// elements of S[q+1].  Stages are separated by scheduling barriers and each
-// stage's VALU results are pinned with empty asm statements, so at most three
-// fragments are live and every MFMA is followed by independent VALU work.
-// kx / vx are this lane's LDS byte offsets of its K row chunk (k-step 0) and
-// of its V^T row chunk (d block 0, slot group 0).
-template <int D, bool MASK>
-__device__ __forceinline__ float half_step(const f32x16& s_cur, f32x16& s_next, f32x16 (&o)[D / 32],
-                                           const bf16x8 (&qf)[D / 16], const char* khalf, const char* vtile,
-                                           int kx, int vx, float m, float& l,
-                                           float sl2, int key_next0, int lo, int hi, int hf) {
-  constexpr int NA = D / 16;        // QK^T MFMAs (k-steps) per half-step
-  constexpr int NB = 2 * (D / 32);  // PV MFMAs per half-step
+// Phase M of one 64-key tile.  QK: S(t+1) = K(t+1) Q^T from the K tile at kt
+// (two halves into s[0], s[1]).  PV: O^T += V(t)^T P(t) from the V tile at vt.
+// kx / vx: this lane's LDS byte offsets of its K row chunk and of its V^T row
+// chunk.  Fragment reads run DIST products ahead of their use.
+template <int D, bool QK, bool PV>
+__device__ __forceinline__ void m_phase(f32x16 (&s)[2], f32x16 (&o)[D / 32], const bf16x8 (&qf)[D / 16],
+                                        const bf16x8 (&pf)[4], const char* kt, const char* vt, int kx, int vx) {
+  using G = Geo<D>;
+  constexpr int KS = D / 16;
   constexpr int DB = D / 32;
-  constexpr int EA = 16 / NA;       // S[q] elements per [A] stage
-  constexpr int EB = 16 / NB;       // S[q+1] elements per [B] stage
-  typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
-  const bf16x2v ones = {(__bf16)1.0f, (__bf16)1.0f};
-  const float nm = -m;
-  bf16x8 pf[2];
-  bf16x8 frag[3];
-  float lsum[2] = {0.f, 0.f};
-  auto kaddr = [&](int ks) { return (const bf16x8*)(khalf + kx + 32 * ks); };
-  frag[0] = *kaddr(0);
-  frag[1] = *kaddr(1);
+  static_assert(4 * DB == 2 * KS, "two PV products per k-step");
+  // Products in issue order: per k-step ks, [S_a(ks), S_b(ks)] then [PV(2ks), PV(2ks+1)].
+  constexpr int PER = (QK ? 2 : 0) + (PV ? 2 : 0);
+  constexpr int N = PER * KS;
+  constexpr int DIST = 3;
+  auto is_qk = [&](int i) { return QK && (i % PER) < 2; };
+  auto frag = [&](int i) -> bf16x8 {
+    const int ks = i / PER, r = i % PER;
+    if (is_qk(i)) return *(const bf16x8*)(kt + r * G::KHALF + kx + 32 * ks);
+    const int j = 2 * ks + (r - (QK ? 2 : 0));  // PV product j: key step j / DB, d block j % DB
+    const int kk = j / DB, db = j % DB;
+    const int half = kk >> 1, k = kk & 1;
+    return *(const bf16x8*)(vt + vx + 16 * (4 * half + k) + db * 32 * G::VROW);
+  };
+  bf16x8 fr[DIST + 1];
 #pragma unroll
-  for (int i = 0; i < NA; ++i) {
-    if (i + 2 < NA) frag[(i + 2) % 3] = *kaddr(i + 2);
-    if (i == 0) {
-      f32x16 z;
+  for (int i = 0; i < DIST; ++i) fr[i] = frag(i);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) z[e] = 0.f;
-      s_next = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag[0], qf[0], z, 0, 0, 0);
-    } else {
-      s_next = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag[i % 3], qf[i], s_next, 0, 0, 0);
-    }
+  for (int i = 0; i < N; ++i) {
+    if (i + DIST < N) fr[(i + DIST) % (DIST + 1)] = frag(i + DIST);
+    const bf16x8 f = fr[i % (DIST + 1)];
+    const int ks = i / PER, r = i % PER;
+    if (is_qk(i)) {
+      if (ks == 0) {
+        f32x16 z;
 #pragma unroll
-    for (int e = EA * i; e < EA * (i + 1); e += 2) {
-      const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[e], sl2, nm));
-      const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[e + 1], sl2, nm));
-      const bf16x2v pk = {(__bf16)e0, (__bf16)e1};
-      pf[e >> 3][e & 7] = pk[0];
-      pf[e >> 3][(e & 7) + 1] = pk[1];
-      lsum[(e >> 1) & 1] = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, lsum[(e >> 1) & 1], false);
-    }
-    asm volatile("" : "+v"(lsum[0]), "+v"(lsum[1]));
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  l += lsum[0] + lsum[1];
-  auto vaddr = [&](int i) { return (const bf16x8*)(vtile + vx + 16 * (i / DB) + (i % DB) * 32 * Geo<D>::VROW); };
-  frag[0] = *vaddr(0);
-  frag[1] = *vaddr(1);
-  float mx[2] = {-INFINITY, -INFINITY};
-#pragma unroll
-  for (int i = 0; i < NB; ++i) {
-    if (i + 2 < NB) frag[(i + 2) % 3] = *vaddr(i + 2);
-    o[i % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag[i % 3], pf[i / DB], o[i % DB], 0, 0, 0);
-#pragma unroll
-    for (int e = EB * i; e < EB * (i + 1); e += 2) {
-      float a0 = s_next[e], a1 = s_next[e + 1];
-      if constexpr (MASK) {
-        const int key = key_next0 + 16 * hf + e;  // key of S^T element e
-        a0 = (key >= lo && key < hi) ? a0 : -INFINITY;
-        a1 = (key + 1 >= lo && key + 1 < hi) ? a1 : -INFINITY;
-        s_next[e] = a0;
-        s_next[e + 1] = a1;
+        for (int e = 0; e < 16; ++e) z[e] = 0.f;
+        s[r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, qf[0], z, 0, 0, 0);
+      } else {
+        s[r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, qf[ks], s[r], 0, 0, 0);
       }
-      mx[(e >> 1) & 1] = fmaxf(mx[(e >> 1) & 1], fmaxf(a0, a1));
+    } else {
+      const int j = 2 * ks + (r - (QK ? 2 : 0));
+      o[j % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, pf[j / DB], o[j % DB], 0, 0, 0);
     }
-    asm volatile("" : "+v"(mx[0]), "+v"(mx[1]));
     __builtin_amdgcn_sched_barrier(0);
   }
-  return half_max(fmaxf(mx[0], mx[1])) * sl2;
+  // Keep the products in this phase (nothing may sink them past the barrier
+  // into the phase that uses them).
+  if constexpr (QK) asm volatile("" : "+v"(s[0]), "+v"(s[1]));
+  if constexpr (PV) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db) asm volatile("" : "+v"(o[db]));
+  }
 }
 
-// LDS buffers of the DMA kernel.  K half-tiles form a ring of four, V^T tiles
-// are double-buffered.  They are separate __shared__ objects (see the kernel)
-// so the compiler can tell that DMA into one buffer does not alias reads of
-// another.
-struct Bufs {
-  char *kh0, *kh1, *kh2, *kh3, *vbuf0, *vbuf1;
+// Phase V: softmax of S(t+1) (both halves).  MASK: keys outside [lo, hi)
+// (tile-relative key kb + ...) are set to -inf first.
+template <int D, bool MASK>
+__device__ __forceinline__ void v_phase(f32x16 (&s)[2], bf16x8 (&pf)[4], f32x16 (&o)[D / 32], float& m,
+                                        float& l, float sl2, int kb, int lo, int hi, int hf) {
+  typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+  const bf16x2v ones = {(__bf16)1.0f, (__bf16)1.0f};
+  // The wave runs this phase alone on its SIMD's vector unit (the other wave
+  // issues matrix products), so each step is applied to all 32 elements
+  // before the next: independent instructions cover each other's latency.
+  if constexpr (MASK) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int key = kb + HK * h + 16 * hf + e;  // key of S^T element e
+        s[h][e] = (key >= lo && key < hi) ? s[h][e] : -INFINITY;
+      }
+  }
+  float mx[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int h = q >> 1, e0 = 8 * (q & 1);
+    mx[q] = fmaxf(fmaxf(fmaxf(s[h][e0], s[h][e0 + 1]), fmaxf(s[h][e0 + 2], s[h][e0 + 3])),
+                  fmaxf(fmaxf(s[h][e0 + 4], s[h][e0 + 5]), fmaxf(s[h][e0 + 6], s[h][e0 + 7])));
+  }
+  const float mxl = half_max(fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]))) * sl2;
+  maybe_rescale<D>(mxl, m, l, o);
+  const float nm = -m;
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s[h][e] = __builtin_fmaf(s[h][e], sl2, nm);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s[h][e] = __builtin_amdgcn_exp2f(s[h][e]);
+  __builtin_amdgcn_sched_barrier(0);
+  float ls[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int e = 0; e < 16; e += 2) {
+      const bf16x2v pk = {(__bf16)s[h][e], (__bf16)s[h][e + 1]};
+      pf[2 * h + (e >> 3)][e & 7] = pk[0];
+      pf[2 * h + (e >> 3)][(e & 7) + 1] = pk[1];
+      ls[(e >> 1) & 3] = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, ls[(e >> 1) & 3], false);
+    }
+  l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+  // Keep the softmax in this phase.
+  asm volatile("" : "+v"(pf[0]), "+v"(pf[1]), "+v"(pf[2]), "+v"(pf[3]), "+v"(l));
+}
+
+// LDS stages: K tile and V^T tile of each of the three ring slots, as
+// separate __shared__ objects (see the kernel).
+struct Ring {
+  char *k0, *k1, *k2, *v0, *v1, *v2;
+  template <int S>
+  __device__ __forceinline__ char* k() const { return S == 0 ? k0 : S == 1 ? k1 : k2; }
+  template <int S>
+  __device__ __forceinline__ char* v() const { return S == 0 ? v0 : S == 1 ? v1 : v2; }
 };
 
-// One query tile (item) of chunk cd over its 64-key tiles [j0, j1).  slot < 0:
-// the segment is the whole key range and the block writes O (and LSE);
-// otherwise it stores its unnormalised partial result in workspace slot
-// `slot` for the merge kernel.
+template <int N>
+using IC = std::integral_constant<int, N>;
+
+// One query tile (item) of chunk cd over its 64-key tiles [j0, j1); slot as
+// in the other DMA kernel (< 0: final output, else a partial-result slot).
 template <int D>
 __device__ __forceinline__ void segment(const AttnParams& p, const ChunkDesc& cd, int qt, int head, int j0,
-                                        int j1, int slot, const Bufs& bf, const DmaPlan<D>& plan, int wave,
+                                        int j1, int slot, const Ring& rg, const Plan<D>& plan, int wave,
                                         int lane) {
   using G = Geo<D>;
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
-  char* const kh0 = bf.kh0;
-  char* const kh1 = bf.kh1;
-  char* const kh2 = bf.kh2;
-  char* const kh3 = bf.kh3;
-  char* const vbuf0 = bf.vbuf0;
-  char* const vbuf1 = bf.vbuf1;
-  const int lq = lane & 31;  // query column owned by this lane
-  const int hf = lane >> 5;  // 32-lane half
+  const int group = wave >> 2;  // wave-uniform
+  const int gw = wave & 3;
+  const int lq = lane & 31;
+  const int hf = lane >> 5;
   const int qrow = qt * BMD + wave * 32 + lq;
   const int row = cd.q_begin + qrow;
   const bool row_ok = qrow < cd.q_len;
-  // Keys relative to the segment's first tile (logical base kv_begin - lead + 64 j0).
   const int base = BN * j0;
   const int lo = max(cd.lead - base, 0);
   const int hi = min(cd.lead + cd.nkeys, BN * j1) - base;
-  const int nt = (hi + BN - 1) / BN;  // 64-key tiles
-  const int nh = (hi + HK - 1) / HK;  // 32-key half-tiles
+  const int nt = (hi + BN - 1) / BN;  // >= 1
   const float sl2 = p.scale_log2;
-  const int kx = lq * G::KROW + 16 * hf;             // K row lq, chunk hf (k-step 0)
-  const int vx0 = lq * G::VROW + 16 * (2 * hf);      // V^T row lq, keys 16 hf .. (first half of a tile)
-  const int vx1 = lq * G::VROW + 16 * (4 + 2 * hf);  // ... keys 32 + 16 hf .. (second half)
+  const int kx = lq * G::KROW + 16 * hf;
+  const int vx = lq * G::VROW + 16 * (2 * hf);
+  // Whether this wave's latest batch of loads (PW instructions) is in flight.
+  bool pend = false;
 
-  // K half-tiles 0..2 and V tile 0 in flight while Q is fetched
-  Cursor kcur = cursor_at<2 * D>(p, cd, head, base), vcur = kcur;
-  dma_k<D>(p, kcur, plan, kh0, wave);
-  advance<2 * D>(p, head, kcur, HK);
-  if (nh > 1) dma_k<D>(p, kcur, plan, kh1, wave);
-  advance<2 * D>(p, head, kcur, HK);
-  if (nh > 2) dma_k<D>(p, kcur, plan, kh2, wave);
-  advance<2 * D>(p, head, kcur, HK);
-  dma_v<D>(p, vcur, plan, vbuf0, wave);
-  advance<2 * D>(p, head, vcur, BN);
-
+  // Prologue loads: group 1 K(0) -> slot 0, K(1) -> slot 1, K(2) -> slot 2;
+  // group 0 V(0) -> slot 1.  Then the query fragments.
+  Cursor cur = cursor_at<2 * D>(p, cd, head, base);
+  const __amdgpu_buffer_rsrc_t rs = cache_rsrc(group == 1 ? p.k : p.v);
+  if (group == 1) {
+    dma_k<D>(p, rs, cur, plan, rg.k<0>(), gw);
+    advance<2 * D>(p, head, cur, BN);
+    if (nt > 1) dma_k<D>(p, rs, cur, plan, rg.k<1>(), gw);
+    advance<2 * D>(p, head, cur, BN);
+    if (nt > 2) dma_k<D>(p, rs, cur, plan, rg.k<2>(), gw);
+    advance<2 * D>(p, head, cur, BN);
+  } else {
+    dma_v<D>(p, rs, cur, plan, rg.v<1>(), gw);
+    advance<2 * D>(p, head, cur, BN);
+  }
   bf16x8 qf[KS];
   {
     const __bf16* qp = (const __bf16*)p.q + ((int64_t)row * p.H + head) * D;
@@ -753,89 +851,122 @@ __device__ __forceinline__ void segment(const AttnParams& p, const ChunkDesc& cd
   for (int b = 0; b < DB; ++b)
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[b][i] = 0.f;
-  float l = 0.f;
+  f32x16 s[2];
+  bf16x8 pf[4];
+  float m = -INFINITY, l = 0.f;
+
+  auto end_phase = [&]() {
+    if (pend)
+      wait_vmcnt<G::PW>();
+    else
+      wait_vmcnt<0>();
+    barrier();
+  };
+  // Loads issued at the start of phase V(t) (t >= -1), before its vector
+  // work covers their latency (an LDS read after an LDS-DMA load of the same
+  // wave waits for that load): group 0 V(t+2) -> slot t % 3 (vdst), group 1
+  // K(t+4) -> slot (t+1) % 3 (kdst).
+  auto loads = [&](int t, char* vdst, char* kdst) {
+    // The previous batch (issued two phases ago) is complete before the next
+    // one is issued: a CU stalls the issue of LDS-DMA loads once about 40 are
+    // in flight, so each wave keeps at most one batch outstanding.
+    wait_vmcnt<0>();
+    if (group == 0) {
+      pend = t + 2 < nt;
+      if (pend) dma_v<D>(p, rs, cur, plan, vdst, gw);
+    } else {
+      pend = t + 4 < nt;
+      if (pend) dma_k<D>(p, rs, cur, plan, kdst, gw);
+    }
+    advance<2 * D>(p, head, cur, BN);
+    // Consume the page-table read now: a scalar load still in flight would
+    // make every LDS wait of the next phase a full wait.
+    asm volatile("" ::"s"(cur.k1), "s"(cur.v1));
+  };
+
+  // Zero the keys of V tile t (stage t, slot sl) outside [lo, hi) in LDS: P is
+  // zero there, but the cache may hold NaN.  Both groups do it at the same
+  // barrier: group 1 after its M(t-1), group 0 after its V(t-1).
+  auto vedge = [&](int t) { return (t == 0 && lo > 0) || BN * (t + 1) > hi; };
+  auto zero_v = [&](char* vt, int t) {
+    zero_v_outside<D>(vt, t, lo, hi);
+    wait_lgkm0();
+    barrier();
+  };
 
   wait_vmcnt<0>();
-  __syncthreads();
-  if (lo > 0 || BN > hi) {  // tile 0 is an edge tile
-    zero_v_outside<D>(vbuf0, 0, lo, hi);
-    __syncthreads();
-  }
-  // S of half-tile 0 (it holds key lo < 8, so its row maxima are finite)
-  f32x16 sa, sb;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) sa[i] = 0.f;
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    const bf16x8 kf = *(const bf16x8*)(kh0 + kx + 32 * ks);
-    sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sa, 0, 0, 0);
-  }
-  float m;
-  {
-    float mx = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int key = 16 * hf + i;
-      sa[i] = (key >= lo && key < hi) ? sa[i] : -INFINITY;
-      mx = fmaxf(mx, sa[i]);
-    }
-    m = half_max(mx) * sl2;
-  }
-  __syncthreads();  // kh0 is free for half-tile 4
+  barrier();
+  if (group == 1) barrier();  // group 1 runs one phase behind
+  // M(-1): S(0) from K(0) in slot 0.
+  m_phase<D, true, false>(s, o, qf, pf, rg.k<0>(), rg.v<0>(), kx, vx);
+  end_phase();
+  if (group == 1 && vedge(0)) zero_v(rg.v<1>(), 0);
+  // V(-1)
+  loads(-1, rg.v<2>(), rg.k<0>());
+  v_phase<D, true>(s, pf, o, m, l, sl2, 0, lo, hi, hf);
+  end_phase();
+  if (group == 0 && vedge(0)) zero_v(rg.v<1>(), 0);
 
-  // Tile step j: half-steps 2j (S in sa) and 2j+1 (S in sb).  EVEN selects
-  // the ring parity: even j reads K halves in kh1, kh2 and refills kh3, kh0;
-  // odd j reads kh3, kh0 and refills kh1, kh2.  M0 / M1: half-tiles 2j+1 /
-  // 2j+2 need masking.
-  auto step = [&](auto even_tag, auto m0_tag, auto m1_tag, int j) {
-    constexpr bool even = decltype(even_tag)::value;
-    char* const k_a = even ? kh1 : kh3;   // half-tile 2j+1
-    char* const k_b = even ? kh2 : kh0;   // half-tile 2j+2
-    char* const k_f0 = even ? kh3 : kh1;  // receives half-tile 2j+3
-    char* const k_f1 = even ? kh0 : kh2;  // receives half-tile 2j+4
-    char* const vb_cur = even ? vbuf0 : vbuf1;
-    char* const vb_free = even ? vbuf1 : vbuf0;
-    // The wave index passes through an empty asm so that the LDS destinations
-    // (one per buffer and instruction) are formed at their use instead of being
-    // hoisted into long-lived scalar registers.
-    int wv = wave;
-    asm volatile("" : "+s"(wv));
-    if (2 * j + 3 < nh) dma_k<D>(p, kcur, plan, k_f0, wv);
-    advance<2 * D>(p, head, kcur, HK);
-    if (2 * j + 4 < nh) dma_k<D>(p, kcur, plan, k_f1, wv);
-    advance<2 * D>(p, head, kcur, HK);
-    if (j + 1 < nt) dma_v<D>(p, vcur, plan, vb_free, wv);
-    advance<2 * D>(p, head, vcur, BN);
-    if (j > 0 && 64 * j + 64 > hi) {  // edge tile (tile 0 was handled before the loop)
-      zero_v_outside<D>(vb_cur, j, lo, hi);
-      __syncthreads();
-    }
-    float mx = half_step<D, decltype(m0_tag)::value>(sa, sb, o, qf, k_a, vb_cur, kx, vx0, m, l,
-                                                     sl2, (2 * j + 1) * HK, lo, hi, hf);
-    if (2 * j + 1 < nh) {
-      maybe_rescale<D>(mx, m, l, o);
-      mx = half_step<D, decltype(m1_tag)::value>(sb, sa, o, qf, k_b, vb_cur, kx, vx1, m, l,
-                                                 sl2, (2 * j + 2) * HK, lo, hi, hf);
-      if (2 * j + 2 < nh) maybe_rescale<D>(mx, m, l, o);
-    }
-    wait_vmcnt<0>();
-    __syncthreads();
+  // Tile t uses stage t in slot (t + 1) % 3.  The loop is unrolled by three
+  // so that every slot is a compile-time constant (the compiler can then tell
+  // the LDS-DMA targets from the buffers being read); every call site below
+  // has a static ring position.  steady(t) needs t + 2 < nt: S(t+1) needs no
+  // mask and V tile t+1 no zeroing.  edge_step(t) is tile nt - 2, last() tile
+  // nt - 1.
+  auto steady = [&](auto rho_tag, int t) {
+    constexpr int rho = decltype(rho_tag)::value;
+    constexpr int sl = (rho + 1) % 3;
+    m_phase<D, true, true>(s, o, qf, pf, rg.k<sl>(), rg.v<sl>(), kx, vx);
+    end_phase();
+    loads(t, rg.v<rho>(), rg.k<sl>());
+    v_phase<D, false>(s, pf, o, m, l, sl2, 0, lo, hi, hf);
+    end_phase();
   };
-  using T_ = std::true_type;
-  using F_ = std::false_type;
-  // Half-tiles q >= 1 need masking iff they reach past hi (lo < 8 only affects
-  // half-tile 0, masked before the loop): iff q >= qe.
-  const int qe = hi / HK;
-  auto dispatch = [&](auto even_tag, int j) {
-    if (2 * j + 2 < qe)
-      step(even_tag, F_{}, F_{}, j);
-    else
-      step(even_tag, T_{}, T_{}, j);
+  auto edge_step = [&](auto rho_tag, int t) {
+    constexpr int rho = decltype(rho_tag)::value;
+    constexpr int sl = (rho + 1) % 3;
+    constexpr int sn = (rho + 2) % 3;  // slot of stage t + 1
+    m_phase<D, true, true>(s, o, qf, pf, rg.k<sl>(), rg.v<sl>(), kx, vx);
+    end_phase();
+    const bool ze = vedge(t + 1);
+    if (group == 1 && ze) zero_v(rg.v<sn>(), t + 1);
+    loads(t, rg.v<rho>(), rg.k<sl>());
+    v_phase<D, true>(s, pf, o, m, l, sl2, BN * (t + 1), lo, hi, hf);
+    end_phase();
+    if (group == 0 && ze) zero_v(rg.v<sn>(), t + 1);
   };
-  for (int j = 0; j < nt; j += 2) {
-    dispatch(T_{}, j);
-    if (j + 1 < nt) dispatch(F_{}, j + 1);
+  auto last = [&](auto rho_tag) {
+    constexpr int sl = (decltype(rho_tag)::value + 1) % 3;
+    m_phase<D, false, true>(s, o, qf, pf, rg.k<sl>(), rg.v<sl>(), kx, vx);
+    end_phase();
+  };
+  int t = 0;
+  for (; t + 4 < nt; t += 3) {
+    steady(IC<0>{}, t);
+    steady(IC<1>{}, t + 1);
+    steady(IC<2>{}, t + 2);
   }
+  switch (nt - t) {  // 1 .. 4 tiles left, t % 3 == 0
+    case 1:
+      last(IC<0>{});
+      break;
+    case 2:
+      edge_step(IC<0>{}, t);
+      last(IC<1>{});
+      break;
+    case 3:
+      steady(IC<0>{}, t);
+      edge_step(IC<1>{}, t + 1);
+      last(IC<2>{});
+      break;
+    default:
+      steady(IC<0>{}, t);
+      steady(IC<1>{}, t + 1);
+      edge_step(IC<2>{}, t + 2);
+      last(IC<0>{});
+      break;
+  }
+  if (group == 0) barrier();  // matches group 1's last M phase
 
   const float lt = half_sum(l);
   if (slot < 0) {
@@ -870,24 +1001,22 @@ __device__ __forceinline__ void segment(const AttnParams& p, const ChunkDesc& cd
 }
 
 template <int D>
-__global__ __launch_bounds__(NTD, 2) void attn_fwd_dma_kernel(const AttnParams p) {
+__global__ __launch_bounds__(NTD, 2) void attn_fwd_pp_kernel(const AttnParams p) {
   using G = Geo<D>;
-  __shared__ __align__(1024) char kh0[G::KHALF];
-  __shared__ __align__(1024) char kh1[G::KHALF];
-  __shared__ __align__(1024) char kh2[G::KHALF];
-  __shared__ __align__(1024) char kh3[G::KHALF];
-  __shared__ __align__(1024) char vbuf0[G::VTILE];
-  __shared__ __align__(1024) char vbuf1[G::VTILE];
-  const Bufs bf{kh0, kh1, kh2, kh3, vbuf0, vbuf1};
-
+  __shared__ __align__(1024) char k0[G::KTILE];
+  __shared__ __align__(1024) char k1[G::KTILE];
+  __shared__ __align__(1024) char k2[G::KTILE];
+  __shared__ __align__(1024) char v0[G::VTILE];
+  __shared__ __align__(1024) char v1[G::VTILE];
+  __shared__ __align__(1024) char v2[G::VTILE];
+  const Ring rg{k0, k1, k2, v0, v1, v2};
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const DmaPlan<D> plan = make_plan<D>(wave, lane, p.P);
-
+  const Plan<D> plan = make_plan<D>(wave >> 2, wave & 3, lane, p.P);
   walk_segments(p, (int)blockIdx.x, [&](int item, int j0, int j1, int slot) {
     const Item it = decode_item(p, item);
-    segment<D>(p, p.chunk[it.c], it.qt, it.head, j0, j1, slot, bf, plan, wave, lane);
+    segment<D>(p, p.chunk[it.c], it.qt, it.head, j0, j1, slot, rg, plan, wave, lane);
   });
 }
 
@@ -947,7 +1076,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const AttnParams p) {
   }
 }
 
-}  // namespace dma
+}  // namespace pp
 
 // ---------------------------------------------------------------------------
 // fp32 kernel (tight-tolerance path): V_MFMA_F32_32X32X2_F32, 32-key tiles,
@@ -1090,18 +1219,18 @@ hipError_t launch_staged_t(const AttnParams& p, hipStream_t s) {
 
 hipError_t launch_attn_bf16_dma(const AttnParams& p, int head_dim, int grid, hipStream_t s) {
   if (head_dim == 128)
-    hipLaunchKernelGGL(dma::attn_fwd_dma_kernel<128>, dim3(grid), dim3(dma::NTD), 0, s, p);
+    hipLaunchKernelGGL(pp::attn_fwd_pp_kernel<128>, dim3(grid), dim3(pp::NTD), 0, s, p);
   else
-    hipLaunchKernelGGL(dma::attn_fwd_dma_kernel<64>, dim3(grid), dim3(dma::NTD), 0, s, p);
+    hipLaunchKernelGGL(pp::attn_fwd_pp_kernel<64>, dim3(grid), dim3(pp::NTD), 0, s, p);
   return hipGetLastError();
 }
 
 hipError_t launch_attn_merge(const AttnParams& p, int head_dim, hipStream_t s) {
   const dim3 grid(p.num_items * (kBlockMDma / kMergeRows));
   if (head_dim == 128)
-    hipLaunchKernelGGL(dma::attn_merge_kernel<128>, grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL(pp::attn_merge_kernel<128>, grid, dim3(256), 0, s, p);
   else
-    hipLaunchKernelGGL(dma::attn_merge_kernel<64>, grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL(pp::attn_merge_kernel<64>, grid, dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
@@ -1111,8 +1240,8 @@ hipError_t attn_dma_resident_blocks(int head_dim, int* blocks) {
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e == hipSuccess)
     e = head_dim == 128
-            ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, dma::attn_fwd_dma_kernel<128>, dma::NTD, 0)
-            : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, dma::attn_fwd_dma_kernel<64>, dma::NTD, 0);
+            ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, pp::attn_fwd_pp_kernel<128>, pp::NTD, 0)
+            : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, pp::attn_fwd_pp_kernel<64>, pp::NTD, 0);
   *blocks = cus * (per_cu > 0 ? per_cu : 1);
   return e;
 }
