@@ -728,16 +728,23 @@ __device__ __forceinline__ void m_phase(f32x16 (&s)[2], f32x16 (&o)[D / 32], con
   }
 }
 
-// Phase V: softmax of S(t+1) (both halves).  MASK: keys outside [lo, hi)
-// (tile-relative key kb + ...) are set to -inf first.
-template <int D, bool MASK>
+// Phase V: softmax of S(t+1) (both 32-key halves, 32 elements per lane).
+//
+// The reference point m of the online softmax is moved only when needed: P is
+// formed with the current m, and only if some lane's partial row sum exceeds
+// 2^11 (so some p > 2^6, i.e. a score more than 6 above m) is the row
+// maximum taken and O, l rescaled exactly before P is formed again.  Every
+// p stays below 2^12 (no overflow; bf16 keeps its relative precision), and
+// the common path needs no maximum.  FIRST: the first tile of a segment sets
+// m from its own row maxima.  MASK: keys outside [lo, hi) (tile-relative key
+// kb + ...) are set to -inf first.  The wave runs this phase alone on its
+// SIMD's vector unit, so each step is applied to all 32 elements before the
+// next: independent instructions cover each other's latency.
+template <int D, bool MASK, bool FIRST>
 __device__ __forceinline__ void v_phase(f32x16 (&s)[2], bf16x8 (&pf)[4], f32x16 (&o)[D / 32], float& m,
                                         float& l, float sl2, int kb, int lo, int hi, int hf) {
   typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
   const bf16x2v ones = {(__bf16)1.0f, (__bf16)1.0f};
-  // The wave runs this phase alone on its SIMD's vector unit (the other wave
-  // issues matrix products), so each step is applied to all 32 elements
-  // before the next: independent instructions cover each other's latency.
   if constexpr (MASK) {
 #pragma unroll
     for (int h = 0; h < 2; ++h)
@@ -747,37 +754,62 @@ __device__ __forceinline__ void v_phase(f32x16 (&s)[2], bf16x8 (&pf)[4], f32x16 
         s[h][e] = (key >= lo && key < hi) ? s[h][e] : -INFINITY;
       }
   }
-  float mx[4];
+  auto row_max = [&]() {
+    float mx[4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int h = q >> 1, e0 = 8 * (q & 1);
-    mx[q] = fmaxf(fmaxf(fmaxf(s[h][e0], s[h][e0 + 1]), fmaxf(s[h][e0 + 2], s[h][e0 + 3])),
-                  fmaxf(fmaxf(s[h][e0 + 4], s[h][e0 + 5]), fmaxf(s[h][e0 + 6], s[h][e0 + 7])));
-  }
-  const float mxl = half_max(fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]))) * sl2;
-  maybe_rescale<D>(mxl, m, l, o);
-  const float nm = -m;
-#pragma unroll
-  for (int h = 0; h < 2; ++h)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) s[h][e] = __builtin_fmaf(s[h][e], sl2, nm);
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int h = 0; h < 2; ++h)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) s[h][e] = __builtin_amdgcn_exp2f(s[h][e]);
-  __builtin_amdgcn_sched_barrier(0);
-  float ls[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int h = 0; h < 2; ++h)
-#pragma unroll
-    for (int e = 0; e < 16; e += 2) {
-      const bf16x2v pk = {(__bf16)s[h][e], (__bf16)s[h][e + 1]};
-      pf[2 * h + (e >> 3)][e & 7] = pk[0];
-      pf[2 * h + (e >> 3)][(e & 7) + 1] = pk[1];
-      ls[(e >> 1) & 3] = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, ls[(e >> 1) & 3], false);
+    for (int q = 0; q < 4; ++q) {
+      const int h = q >> 1, e0 = 8 * (q & 1);
+      float a = fmaxf(s[h][e0], fmaxf(s[h][e0 + 1], s[h][e0 + 2]));
+      a = fmaxf(a, fmaxf(s[h][e0 + 3], s[h][e0 + 4]));
+      a = fmaxf(a, fmaxf(s[h][e0 + 5], s[h][e0 + 6]));
+      mx[q] = fmaxf(a, s[h][e0 + 7]);
     }
-  l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+    return half_max(fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]))) * sl2;
+  };
+  // P = exp2(S sl2 - m) into pf; returns this lane's sum of the bf16 values.
+  auto form_p = [&]() {
+    const float nm = -m;
+    float e[2][16];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int k = 0; k < 16; ++k) e[h][k] = __builtin_fmaf(s[h][k], sl2, nm);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int k = 0; k < 16; ++k) e[h][k] = __builtin_amdgcn_exp2f(e[h][k]);
+    __builtin_amdgcn_sched_barrier(0);
+    float ls[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int k = 0; k < 16; k += 2) {
+        const bf16x2v pk = {(__bf16)e[h][k], (__bf16)e[h][k + 1]};
+        pf[2 * h + (k >> 3)][k & 7] = pk[0];
+        pf[2 * h + (k >> 3)][(k & 7) + 1] = pk[1];
+        ls[(k >> 1) & 3] = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, ls[(k >> 1) & 3], false);
+      }
+    return (ls[0] + ls[1]) + (ls[2] + ls[3]);
+  };
+  if constexpr (FIRST) {
+    m = row_max();
+    l = 0.f;
+  }
+  float lsum = form_p();
+  if (!FIRST && __builtin_expect(__builtin_amdgcn_ballot_w64(!(lsum <= 2048.f)) != 0, 0)) {
+    asm volatile("");  // a real branch: the recomputation must not be executed speculatively
+    const float m_new = fmaxf(m, row_max());
+    const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+    m = m_new;
+    l *= alpha;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+    lsum = form_p();
+  }
+  l += lsum;
   // Keep the softmax in this phase.
   asm volatile("" : "+v"(pf[0]), "+v"(pf[1]), "+v"(pf[2]), "+v"(pf[3]), "+v"(l));
 }
@@ -903,7 +935,7 @@ __device__ __forceinline__ void segment(const AttnParams& p, const ChunkDesc& cd
   if (group == 1 && vedge(0)) zero_v(rg.v<1>(), 0);
   // V(-1)
   loads(-1, rg.v<2>(), rg.k<0>());
-  v_phase<D, true>(s, pf, o, m, l, sl2, 0, lo, hi, hf);
+  v_phase<D, true, true>(s, pf, o, m, l, sl2, 0, lo, hi, hf);
   end_phase();
   if (group == 0 && vedge(0)) zero_v(rg.v<1>(), 0);
 
@@ -919,7 +951,7 @@ __device__ __forceinline__ void segment(const AttnParams& p, const ChunkDesc& cd
     m_phase<D, true, true>(s, o, qf, pf, rg.k<sl>(), rg.v<sl>(), kx, vx);
     end_phase();
     loads(t, rg.v<rho>(), rg.k<sl>());
-    v_phase<D, false>(s, pf, o, m, l, sl2, 0, lo, hi, hf);
+    v_phase<D, false, false>(s, pf, o, m, l, sl2, 0, lo, hi, hf);
     end_phase();
   };
   auto edge_step = [&](auto rho_tag, int t) {
@@ -931,7 +963,7 @@ __device__ __forceinline__ void segment(const AttnParams& p, const ChunkDesc& cd
     const bool ze = vedge(t + 1);
     if (group == 1 && ze) zero_v(rg.v<sn>(), t + 1);
     loads(t, rg.v<rho>(), rg.k<sl>());
-    v_phase<D, true>(s, pf, o, m, l, sl2, BN * (t + 1), lo, hi, hf);
+    v_phase<D, true, false>(s, pf, o, m, l, sl2, BN * (t + 1), lo, hi, hf);
     end_phase();
     if (group == 0 && ze) zero_v(rg.v<sn>(), t + 1);
   };
