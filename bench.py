@@ -57,8 +57,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=4680, help="query rows in the oracle timing sample")
     ap.add_argument("--schedule", default="balanced", choices=["balanced", "tile"],
-                    help="attention schedule: balanced shares of (query tile x key tile) steps with a "
-                         "merge of split tiles (needs a workspace), or one workgroup per query tile")
+                    help="balanced: pass a workspace, so the library may choose its split schedule (key "
+                         "parts merged by log-sum-exp) where it applies; tile: no workspace, one workgroup "
+                         "per query tile.  The JSON line reports the schedule the library took")
     ap.add_argument("--quantize-append", action="store_true",
                     help="fp8round: new K/V arrive as bf16 and the append quantises them to E4M3FN "
                          "(wf_kv_append_quantize) instead of copying pre-quantised pages")
@@ -189,9 +190,12 @@ def run_round(args, cfg):
                 marks.append((e0, e1, e2, c.end - kb))
         return marks
 
-    for _ in range(args.warmup):
+    for _ in range(max(1, args.warmup)):
         step(False)
     torch.cuda.synchronize()
+    c0 = layers[0].cache
+    plan = wf.wf_chunk_attn_plan(c0, [0, n], [max(c0.start, c0.end - WINDOW)], [c0.end], "bf16",
+                                 0 if ws is None else ws.numel())
     t_start, t_end = ev(), ev()
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
@@ -238,7 +242,7 @@ def run_round(args, cfg):
                      graph_tflops=round(flops_per_launch * cfg["layers"] / (gms * 1e-3) / 1e12, 2),
                      graph_phases=rr.period)
     return dict(
-        graph=graph,
+        plan=plan, graph=graph,
         ms_per_step=ms_step, wall_s=wall, value=total_flops / (total_ms * 1e-3) / 1e12,
         attn_kernel_ms=avg_att, attn_tflops=flops_per_launch / (avg_att * 1e-3) / 1e12, att_ms=att_ms,
         append_kernel_ms=avg_app, append_gbps=app_bytes / (avg_app * 1e-3) / 1e9, app_ms=app_ms,
@@ -269,6 +273,7 @@ def run_single(args, cfg, wave):
         q_off, kb, ke = [0, CHUNK], [0], [4 * CHUNK]
         flops = attn_flops(H, D, CHUNK, 4 * CHUNK)
     ws = wf.workspace_for(cache, "cuda") if args.schedule == "balanced" else None
+    plan = wf.wf_chunk_attn_plan(cache, q_off, kb, ke, "bf16", 0 if ws is None else ws.numel())
     for _ in range(args.warmup):
         wf.wf_chunk_attn_fwd(cache, q, q_off, kb, ke, o=o, workspace=ws)
     torch.cuda.synchronize()
@@ -282,7 +287,7 @@ def run_single(args, cfg, wave):
     wall = time.perf_counter() - t0
     ms = [a.elapsed_time(b) for a, b in evs]
     avg = sum(ms) / len(ms)
-    return dict(ms_per_step=avg, wall_s=wall, value=flops / (avg * 1e-3) / 1e12, attn_kernel_ms=avg,
+    return dict(plan=plan, ms_per_step=avg, wall_s=wall, value=flops / (avg * 1e-3) / 1e12, attn_kernel_ms=avg,
                 attn_tflops=flops / (avg * 1e-3) / 1e12, flops_per_launch=flops, H=H, D=D, layers=1, att_ms=ms,
                 append_kernel_ms=None, append_gbps=None, chunks_per_s=None, append_bytes=None, app_ms=None)
 
@@ -357,7 +362,8 @@ def main():
         "data": "synthetic (seeded N(0, s^2) on device, random page tables)",
         "config": {"workload": cfg["name"], "layers": cfg["layers"], "heads": r["H"], "head_dim": r["D"],
                    "query_rows": cfg.get("chunk", CHUNK), "keys": WINDOW if "round" in args.workload else None,
-                   "parallelism": "single GPU", "schedule": args.schedule},
+                   "parallelism": "single GPU", "schedule": r["plan"]["schedule"],
+                   "attn_grid": r["plan"]["grid"]},
         "pct_bf16_peak": round(100.0 * r["value"] / BF16_PEAK_TFLOPS, 2),
         "attn_kernel_tflops": round(r["attn_tflops"], 2),
         "attn_kernel_ms": round(r["attn_kernel_ms"], 4),

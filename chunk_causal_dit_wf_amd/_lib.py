@@ -50,6 +50,14 @@ class wf_kv_cache(ctypes.Structure):
     ]
 
 
+class wf_attn_plan(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("kernel", "schedule", "grid", "items", "rows_per_item", "parts",
+                                               "tail_tiles", "tails_per_block")]
+
+
+KERNEL_NAMES = {0: "f32", 1: "staged_bf16", 2: "staged_fp8", 3: "dma_bf16", 4: "dma_fp8"}
+SCHEDULE_NAMES = {0: "per_tile", 1: "split"}
+
 _lib = None
 
 
@@ -70,8 +78,10 @@ def lib():
         L.wf_chunk_attn_fwd.argtypes = [P, vp, i32, vp, vp, i32, ctypes.POINTER(i32), ctypes.POINTER(i64),
                                         ctypes.POINTER(i64), f32, vp, ctypes.c_uint64, vp]
         L.wf_chunk_attn_workspace_bytes.argtypes = [P, ctypes.POINTER(ctypes.c_uint64)]
+        L.wf_chunk_attn_plan.argtypes = [P, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i64), ctypes.POINTER(i64),
+                                         ctypes.c_uint64, ctypes.POINTER(wf_attn_plan)]
         for name in ("wf_kv_cache_check", "wf_kv_cache_bytes", "wf_kv_append", "wf_kv_evict", "wf_chunk_attn_fwd",
-                     "wf_chunk_attn_workspace_bytes", "wf_kv_append_quantize"):
+                     "wf_chunk_attn_workspace_bytes", "wf_kv_append_quantize", "wf_chunk_attn_plan"):
             getattr(L, name).restype = ctypes.c_int
         L.wf_last_error.restype = ctypes.c_char_p
         L.wf_last_error.argtypes = []
@@ -203,12 +213,7 @@ def wf_chunk_attn_fwd(cache, q, q_off, kv_begin, kv_end, softmax_scale=0.0, o=No
     qo = (ctypes.c_int32 * (nc + 1))(*[int(x) for x in q_off])
     kb = (ctypes.c_int64 * nc)(*[int(x) for x in kv_begin])
     ke = (ctypes.c_int64 * nc)(*[int(x) for x in kv_end])
-    if q.dtype == torch.float32:
-        qd = WF_F32
-    elif q.dtype == torch.bfloat16:
-        qd = WF_BF16
-    else:
-        raise WfError(WF_ERR_UNSUPPORTED, "q dtype %s" % q.dtype)
+    qd = _q_dtype(q)
     if o is None:
         o = torch.empty_like(q)
     if lse is None and return_lse:
@@ -219,6 +224,29 @@ def wf_chunk_attn_fwd(cache, q, q_off, kv_begin, kv_end, softmax_scale=0.0, o=No
     _check(lib().wf_chunk_attn_fwd(ctypes.byref(cache.c), _ptr(q), qd, _ptr(o), _ptr(lse), nc, qo, kb, ke,
                                    float(softmax_scale), _ptr(workspace), wsb, _stream(stream)))
     return (o, lse) if lse is not None else o
+
+
+def _q_dtype(q):
+    if q.dtype == torch.float32:
+        return WF_F32
+    if q.dtype == torch.bfloat16:
+        return WF_BF16
+    raise WfError(WF_ERR_UNSUPPORTED, "q dtype %s" % q.dtype)
+
+
+def wf_chunk_attn_plan(cache, q_off, kv_begin, kv_end, q_dtype="bf16", workspace_bytes=0):
+    """The launch wf_chunk_attn_fwd would make (kernel, schedule, grid, ...), as a dict."""
+    nc = len(kv_begin)
+    qo = (ctypes.c_int32 * (nc + 1))(*[int(x) for x in q_off])
+    kb = (ctypes.c_int64 * nc)(*[int(x) for x in kv_begin])
+    ke = (ctypes.c_int64 * nc)(*[int(x) for x in kv_end])
+    out = wf_attn_plan()
+    _check(lib().wf_chunk_attn_plan(ctypes.byref(cache.c), DTYPE_CODES[q_dtype], nc, qo, kb, ke,
+                                    int(workspace_bytes), ctypes.byref(out)))
+    d = {n: getattr(out, n) for n, _ in wf_attn_plan._fields_}
+    d["kernel"] = KERNEL_NAMES[d["kernel"]]
+    d["schedule"] = SCHEDULE_NAMES[d["schedule"]]
+    return d
 
 
 def version():

@@ -335,10 +335,13 @@ wf_status wf_chunk_attn_workspace_bytes(const wf_kv_cache* c, uint64_t* bytes) {
   return ok();
 }
 
-wf_status wf_chunk_attn_fwd(const wf_kv_cache* c, const void* q, int32_t q_dtype, void* o, float* lse,
-                            int32_t num_chunks, const int32_t* q_off, const int64_t* kv_begin,
-                            const int64_t* kv_end, float softmax_scale, void* workspace,
-                            uint64_t workspace_bytes, void* stream) {
+// Validation of the chunk tables and the whole launch plan of an attention
+// call: kernel, item table, schedule and grid.  Needs the device (resident
+// workgroup count) only when a workspace is given.  Fills p except for the
+// q / o / lse / ws pointers.
+static wf_status plan_attention(const wf_kv_cache* c, int32_t q_dtype, int32_t num_chunks, const int32_t* q_off,
+                                const int64_t* kv_begin, const int64_t* kv_end, float softmax_scale,
+                                uint64_t workspace_bytes, wf::AttnParams& p, wf_attn_plan& L) {
   wf_status s = check_layout(c);
   if (s != WF_OK) return s;
   if ((s = check_window(c)) != WF_OK) return s;
@@ -363,35 +366,9 @@ wf_status wf_chunk_attn_fwd(const wf_kv_cache* c, const void* q, int32_t q_dtype
   if (nq * c->num_heads >= ((int64_t)1 << 31))
     return fail(WF_ERR_UNSUPPORTED, "too many query rows (%lld x %d heads)", (long long)nq, c->num_heads);
   if (!(std::isfinite(softmax_scale))) return fail(WF_ERR_INVALID_ARG, "softmax_scale is not finite");
-  if (nq == 0) return ok();
-  if (q == nullptr || o == nullptr) return fail(WF_ERR_INVALID_ARG, "q/o is NULL");
-  if (!aligned(q, 16) || !aligned(o, 16)) return fail(WF_ERR_INVALID_ARG, "q/o must be 16-byte aligned");
-  if (lse != nullptr && !aligned(lse, 4)) return fail(WF_ERR_INVALID_ARG, "lse must be 4-byte aligned");
-  const uint64_t qb = (uint64_t)nq * c->num_heads * c->head_dim * esize_of(q_dtype);
-  const uint64_t kvb = kv_bytes_of(c);
-  if (overlap(o, qb, q, qb) || overlap(o, qb, c->k, kvb) || overlap(o, qb, c->v, kvb))
-    return fail(WF_ERR_INVALID_ARG, "o overlaps q or the cache");
-  const uint64_t lb = lse != nullptr ? (uint64_t)nq * c->num_heads * 4 : 0;
-  if (lse != nullptr) {
-    if (overlap(lse, lb, o, qb) || overlap(lse, lb, q, qb) || overlap(lse, lb, c->k, kvb) ||
-        overlap(lse, lb, c->v, kvb))
-      return fail(WF_ERR_INVALID_ARG, "lse overlaps q, o or the cache");
-  }
-  if ((workspace == nullptr) != (workspace_bytes == 0))
-    return fail(WF_ERR_INVALID_ARG, "workspace and workspace_bytes must both be set or both be 0");
-  if (workspace != nullptr) {
-    if (!aligned(workspace, 256)) return fail(WF_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-    if (overlap(workspace, workspace_bytes, q, qb) || overlap(workspace, workspace_bytes, o, qb) ||
-        overlap(workspace, workspace_bytes, c->k, kvb) || overlap(workspace, workspace_bytes, c->v, kvb) ||
-        (lse != nullptr && overlap(workspace, workspace_bytes, lse, lb)))
-      return fail(WF_ERR_INVALID_ARG, "workspace overlaps another argument");
-  }
 
-  wf::AttnParams p;
   std::memset(&p, 0, sizeof(p));
-  p.q = q;
-  p.o = o;
-  p.lse = lse;
+  std::memset(&L, 0, sizeof(L));
   p.k = c->k;
   p.v = c->v;
   p.ks = c->k_scale;
@@ -406,13 +383,19 @@ wf_status wf_chunk_attn_fwd(const wf_kv_cache* c, const void* q, int32_t q_dtype
   p.divP = wf::make_fastdiv((uint32_t)c->page_size);
   p.divT = wf::make_fastdiv((uint32_t)c->table_len);
   std::memcpy(p.table, c->page_table, sizeof(int32_t) * c->table_len);
-  // The DMA kernel addresses a key tile as at most two page runs with 32-bit
-  // byte offsets: it takes bf16 caches with pages of at least one tile (64
-  // keys) and under 4 GiB.  Everything else goes to the register-staged kernel.
+  // The DMA kernels address a key tile as at most two page runs with 32-bit
+  // byte offsets: they take caches with pages of at least one tile (64 keys)
+  // and under 4 GiB.  Everything else goes to the register-staged kernel.
+  const uint64_t kvb = kv_bytes_of(c);
   const bool use_dma = kvd == WF_BF16 && c->page_size >= 64 && kvb < ((uint64_t)1 << 32);
   bool use_fp8 = kvd == WF_FP8_E4M3 && c->page_size >= 64 && kvb < ((uint64_t)1 << 32);
   for (int i = 0; i < num_chunks && use_fp8; ++i)
     use_fp8 = (kv_begin[i] % 8) + (kv_end[i] - kv_begin[i]) <= (int64_t)8 * wf::kFp8MaxGroups;
+  L.kernel = q_dtype == WF_F32 ? WF_KERNEL_F32
+             : use_dma        ? WF_KERNEL_DMA_BF16
+             : use_fp8        ? WF_KERNEL_DMA_FP8
+             : kvd == WF_BF16 ? WF_KERNEL_STAGED_BF16
+                              : WF_KERNEL_STAGED_FP8;
 
   // Longest-processing-time-first order: chunks with the most (query x key) work are issued first.
   std::vector<int> order;
@@ -423,7 +406,8 @@ wf_status wf_chunk_attn_fwd(const wf_kv_cache* c, const void* q, int32_t q_dtype
     const int64_t wb = (int64_t)(q_off[b + 1] - q_off[b]) * (kv_end[b] - kv_begin[b]);
     return wa > wb;
   });
-  const int block_m = q_dtype == WF_F32 ? wf::kBlockMF32 : (use_dma || use_fp8) ? wf::kBlockMDma : wf::kBlockMStaged;
+  const bool dma = L.kernel == WF_KERNEL_DMA_BF16 || L.kernel == WF_KERNEL_DMA_FP8;
+  const int block_m = q_dtype == WF_F32 ? wf::kBlockMF32 : dma ? wf::kBlockMDma : wf::kBlockMStaged;
   int64_t items = 0;
   int nc = 0;
   for (int i : order) {
@@ -440,34 +424,93 @@ wf_status wf_chunk_attn_fwd(const wf_kv_cache* c, const void* q, int32_t q_dtype
   }
   p.num_chunks = nc;
   p.num_items = (int32_t)items;
-  if (items == 0) return ok();
+  L.items = (int32_t)items;
+  L.rows_per_item = block_m;
+  L.grid = (int32_t)items;
+  L.schedule = WF_SCHED_PER_TILE;
+  L.parts = 1;
+  L.tails_per_block = 0;
+  L.tail_tiles = 0;
+  if (items == 0 || !dma || workspace_bytes == 0) return ok();
+
+  int resident = 0;
+  hipError_t e = L.kernel == WF_KERNEL_DMA_BF16 ? wf::attn_dma_resident_blocks(c->head_dim, &resident)
+                                                : wf::attn_fp8_resident_blocks(c->head_dim, &resident);
+  if (e != hipSuccess) return fail(WF_ERR_HIP, "device query failed: %s", hipGetErrorString(e));
+  const uint64_t need = (uint64_t)2 * resident * wf::ws_slot_floats(c->head_dim) * sizeof(float);
+  if (workspace_bytes < need)
+    return fail(WF_ERR_INVALID_ARG, "workspace of %llu bytes is smaller than the %llu required",
+                (unsigned long long)workspace_bytes, (unsigned long long)need);
+  if (plan_split(p, (int)items, resident)) {
+    L.schedule = WF_SCHED_SPLIT;
+    L.parts = p.sp.m;
+    L.tail_tiles = p.sp.b;
+    L.tails_per_block = p.sp.b > 0 ? p.sp.q : 0;
+    L.grid = p.sp.n * p.sp.m + (p.sp.b > 0 ? (p.sp.n * p.sp.m + p.sp.q - 1) / p.sp.q : 0);
+  }
+  return ok();
+}
+
+wf_status wf_chunk_attn_plan(const wf_kv_cache* c, int32_t q_dtype, int32_t num_chunks, const int32_t* q_off,
+                             const int64_t* kv_begin, const int64_t* kv_end, uint64_t workspace_bytes,
+                             wf_attn_plan* plan) {
+  if (plan == nullptr) return fail(WF_ERR_INVALID_ARG, "plan is NULL");
+  wf::AttnParams p;
+  wf_attn_plan L;
+  wf_status s = plan_attention(c, q_dtype, num_chunks, q_off, kv_begin, kv_end, 0.f, workspace_bytes, p, L);
+  if (s != WF_OK) return s;
+  *plan = L;
+  return ok();
+}
+
+wf_status wf_chunk_attn_fwd(const wf_kv_cache* c, const void* q, int32_t q_dtype, void* o, float* lse,
+                            int32_t num_chunks, const int32_t* q_off, const int64_t* kv_begin,
+                            const int64_t* kv_end, float softmax_scale, void* workspace,
+                            uint64_t workspace_bytes, void* stream) {
+  if ((workspace == nullptr) != (workspace_bytes == 0))
+    return fail(WF_ERR_INVALID_ARG, "workspace and workspace_bytes must both be set or both be 0");
+  if (workspace != nullptr && !aligned(workspace, 256))
+    return fail(WF_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  wf::AttnParams p;
+  wf_attn_plan L;
+  wf_status s = plan_attention(c, q_dtype, num_chunks, q_off, kv_begin, kv_end, softmax_scale, workspace_bytes, p, L);
+  if (s != WF_OK) return s;
+  const int64_t nq = p.nq;
+  if (nq == 0) return ok();
+  if (q == nullptr || o == nullptr) return fail(WF_ERR_INVALID_ARG, "q/o is NULL");
+  if (!aligned(q, 16) || !aligned(o, 16)) return fail(WF_ERR_INVALID_ARG, "q/o must be 16-byte aligned");
+  if (lse != nullptr && !aligned(lse, 4)) return fail(WF_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  const uint64_t qb = (uint64_t)nq * c->num_heads * c->head_dim * esize_of(q_dtype);
+  const uint64_t kvb = kv_bytes_of(c);
+  if (overlap(o, qb, q, qb) || overlap(o, qb, c->k, kvb) || overlap(o, qb, c->v, kvb))
+    return fail(WF_ERR_INVALID_ARG, "o overlaps q or the cache");
+  const uint64_t lb = lse != nullptr ? (uint64_t)nq * c->num_heads * 4 : 0;
+  if (lse != nullptr) {
+    if (overlap(lse, lb, o, qb) || overlap(lse, lb, q, qb) || overlap(lse, lb, c->k, kvb) ||
+        overlap(lse, lb, c->v, kvb))
+      return fail(WF_ERR_INVALID_ARG, "lse overlaps q, o or the cache");
+  }
+  if (workspace != nullptr) {
+    if (overlap(workspace, workspace_bytes, q, qb) || overlap(workspace, workspace_bytes, o, qb) ||
+        overlap(workspace, workspace_bytes, c->k, kvb) || overlap(workspace, workspace_bytes, c->v, kvb) ||
+        (lse != nullptr && overlap(workspace, workspace_bytes, lse, lb)))
+      return fail(WF_ERR_INVALID_ARG, "workspace overlaps another argument");
+  }
+  if (L.items == 0) return ok();
+  p.q = q;
+  p.o = o;
+  p.lse = lse;
+  if (L.schedule == WF_SCHED_SPLIT) p.ws = (float*)workspace;
 
   hipError_t e;
-  if (q_dtype == WF_F32)
-    e = wf::launch_attn_f32(p, c->head_dim, (hipStream_t)stream);
-  else if (use_dma || use_fp8) {
-    int grid = (int)items;
-    if (workspace != nullptr) {
-      int resident = 0;
-      e = use_dma ? wf::attn_dma_resident_blocks(c->head_dim, &resident)
-                  : wf::attn_fp8_resident_blocks(c->head_dim, &resident);
-      if (e != hipSuccess) return fail(WF_ERR_HIP, "device query failed: %s", hipGetErrorString(e));
-      const uint64_t need = (uint64_t)2 * resident * wf::ws_slot_floats(c->head_dim) * sizeof(float);
-      if (workspace_bytes < need)
-        return fail(WF_ERR_INVALID_ARG, "workspace of %llu bytes is smaller than the %llu required",
-                    (unsigned long long)workspace_bytes, (unsigned long long)need);
-      if (plan_split(p, (int)items, resident)) {
-        p.ws = (float*)workspace;
-        grid = p.sp.n * p.sp.m + (p.sp.b > 0 ? (p.sp.n * p.sp.m + p.sp.q - 1) / p.sp.q : 0);
-      }
-    }
-    e = use_dma ? wf::launch_attn_bf16_dma(p, c->head_dim, grid, (hipStream_t)stream)
-                : wf::launch_attn_fp8_dma(p, c->head_dim, grid, (hipStream_t)stream);
-    if (e == hipSuccess && p.ws != nullptr) e = wf::launch_attn_merge(p, c->head_dim, (hipStream_t)stream);
-  } else if (kvd == WF_BF16)
-    e = wf::launch_attn_bf16_staged(p, c->head_dim, (hipStream_t)stream);
-  else
-    e = wf::launch_attn_fp8kv(p, c->head_dim, (hipStream_t)stream);
+  switch (L.kernel) {
+    case WF_KERNEL_F32: e = wf::launch_attn_f32(p, c->head_dim, (hipStream_t)stream); break;
+    case WF_KERNEL_DMA_BF16: e = wf::launch_attn_bf16_dma(p, c->head_dim, L.grid, (hipStream_t)stream); break;
+    case WF_KERNEL_DMA_FP8: e = wf::launch_attn_fp8_dma(p, c->head_dim, L.grid, (hipStream_t)stream); break;
+    case WF_KERNEL_STAGED_BF16: e = wf::launch_attn_bf16_staged(p, c->head_dim, (hipStream_t)stream); break;
+    default: e = wf::launch_attn_fp8kv(p, c->head_dim, (hipStream_t)stream); break;
+  }
+  if (e == hipSuccess && p.ws != nullptr) e = wf::launch_attn_merge(p, c->head_dim, (hipStream_t)stream);
   if (e != hipSuccess) return fail(WF_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
   return ok();
 }

@@ -72,6 +72,10 @@ typedef enum wf_dtype {
  *   v       [num_pages][num_heads][head_dim][page_size]
  *           (per page and head: value rows stored transposed, so the key
  *            index is contiguous -- the layout the P*V product consumes)
+ *   The pages fix no cache layout.  Heads are outermost inside a page (a
+ *   (page, head) block is one contiguous run), and V is transposed once per
+ *   token when it is appended, so that every attention call reads V^T rows
+ *   of consecutive keys instead of gathering them.
  *   k_scale, v_scale   E4M3FN only, float32 [num_pages][num_heads][nblk],
  *           nblk = ceil(page_size / 128); block b of a page covers offsets
  *           [128 b, min(128 (b+1), page_size)).  Value = decode(code) * scale.
@@ -148,7 +152,10 @@ wf_status wf_kv_append_quantize(wf_kv_cache *cache, int64_t pos, int32_t n, cons
                                 const void *v_new, void *stream);
 
 /*
- * Drop the n oldest live tokens: start += n (rolling window).  Requires
+ * Drop the n oldest live tokens: start += n (rolling window).  Source: the
+ * KV-cached loop advances one chunk at a time (scope-causal-forcing README,
+ * "How It Works", step 4) over a bounded, rolling history (the Rolling
+ * Forcing baseline named in the Wave Forcing abstract).  Requires
  * 0 <= n <= end - start.  No kernel is launched unless flags has
  * WF_EVICT_POISON, which overwrites the evicted rows with NaN codes so that a
  * later read of them shows up (a test aid).
@@ -173,14 +180,22 @@ wf_status wf_kv_evict(wf_kv_cache *cache, int32_t n, uint32_t flags, void *strea
  *   workspace, workspace_bytes
  *              optional device scratch (caller-owned, 256-byte aligned, at
  *              least wf_chunk_attn_workspace_bytes() bytes, not overlapping
- *              any other argument).  With a workspace, BF16 caches are
- *              processed by a balanced schedule: the (query tile x key
- *              tile) work is cut into one equal share per resident
- *              workgroup, query tiles cut between shares leave fp32 partial
- *              results in the workspace, and a second kernel merges them by
- *              their log-sum-exp.  NULL (with workspace_bytes 0) selects one
- *              workgroup per query tile.  Calls that share a workspace must
- *              be ordered (same stream).
+ *              any other argument).  NULL (with workspace_bytes 0) selects
+ *              one workgroup per query tile of 256 rows ("per-tile"
+ *              schedule).  With a workspace, calls on the LDS-DMA kernels
+ *              (bf16 or E4M3FN caches with pages of >= 64 tokens) may take
+ *              the split schedule instead: it is used when every chunk spans
+ *              the same number S of 64-key tiles and there are fewer work
+ *              items (query tiles x heads) than resident workgroups.  Each
+ *              item's key tiles are then cut into m = min(resident / items,
+ *              S / 32, 8) parts; workgroups still idle take the last b key
+ *              tiles of q parts each (used only when q <= 5 and b >= 8);
+ *              each part leaves fp32 partial results in the workspace and a
+ *              second kernel merges them by their log-sum-exp (an exact
+ *              re-association of the softmax).  When m = 1 and no tails are
+ *              taken the call runs per-tile even with a workspace.
+ *              wf_chunk_attn_plan() reports the choice.  Calls that share a
+ *              workspace must be ordered (same stream).
  * 1 <= num_chunks <= WF_MAX_CHUNKS.  Accumulation is fp32.  Results are
  * deterministic run to run on a given device and schedule.  Keys outside a
  * chunk's range are never used (NaN there does not leak into the output).
@@ -189,6 +204,44 @@ wf_status wf_chunk_attn_fwd(const wf_kv_cache *cache, const void *q, int32_t q_d
                             float *lse, int32_t num_chunks, const int32_t *q_off,
                             const int64_t *kv_begin, const int64_t *kv_end, float softmax_scale,
                             void *workspace, uint64_t workspace_bytes, void *stream);
+
+/* Attention kernels and schedules, as reported by wf_chunk_attn_plan(). */
+typedef enum wf_attn_kernel {
+  WF_KERNEL_F32 = 0,         /* fp32 Q and cache: fp32 MFMA                       */
+  WF_KERNEL_STAGED_BF16 = 1, /* bf16 cache, pages < 64 tokens (or >= 4 GiB)       */
+  WF_KERNEL_STAGED_FP8 = 2,  /* E4M3FN cache dequantised to bf16 on the way in    */
+  WF_KERNEL_DMA_BF16 = 3,    /* bf16 cache, pages >= 64: LDS-DMA, bf16 MFMA        */
+  WF_KERNEL_DMA_FP8 = 4      /* E4M3FN cache, pages >= 64: LDS-DMA, fp8 MFMA       */
+} wf_attn_kernel;
+
+typedef enum wf_attn_schedule {
+  WF_SCHED_PER_TILE = 0, /* one workgroup per (query tile, head)              */
+  WF_SCHED_SPLIT = 1     /* key-range parts + tails, merged by log-sum-exp     */
+} wf_attn_schedule;
+
+typedef struct wf_attn_plan {
+  int32_t kernel;          /* wf_attn_kernel                                  */
+  int32_t schedule;        /* wf_attn_schedule                                */
+  int32_t grid;            /* workgroups of the attention launch              */
+  int32_t items;           /* query tiles x heads                             */
+  int32_t rows_per_item;   /* query rows per tile                             */
+  int32_t parts;           /* split: key parts per item (1 otherwise)         */
+  int32_t tail_tiles;      /* split: key tiles per tail part (0: no tails)    */
+  int32_t tails_per_block; /* split: tail parts per tail workgroup            */
+} wf_attn_plan;
+
+/*
+ * The launch wf_chunk_attn_fwd would make for these arguments, without
+ * making it: kernel, schedule and grid (a host query, so that callers and
+ * benchmarks can state which path ran).  Arguments as for
+ * wf_chunk_attn_fwd; workspace_bytes is the size of the workspace that
+ * would be passed (0 = none).  Validates the cache and the chunk tables like
+ * wf_chunk_attn_fwd; with workspace_bytes > 0 it queries the current HIP
+ * device (WF_ERR_HIP without one).  Enqueues nothing.
+ */
+wf_status wf_chunk_attn_plan(const wf_kv_cache *cache, int32_t q_dtype, int32_t num_chunks,
+                             const int32_t *q_off, const int64_t *kv_begin, const int64_t *kv_end,
+                             uint64_t workspace_bytes, wf_attn_plan *plan);
 
 /*
  * Workspace bytes wf_chunk_attn_fwd needs for the balanced schedule on the

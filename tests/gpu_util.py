@@ -101,3 +101,47 @@ def errors(got, ref):
     d = np.abs(got - ref)
     rel = np.sqrt((d ** 2).sum() / max((ref ** 2).sum(), 1e-300))
     return float(d.max()), float(d.mean()), float(rel)
+
+
+LOG2E = 1.4426950408889634
+
+
+def rescale_events(q_vals, k_vals, kb, ke, kind, scale=None):
+    """Key tiles at which the online softmax of the attention kernels must move its
+    reference point, derived from the inputs alone (one head).
+
+    q_vals [R, D] query rows, k_vals [ke - kb, D] the keys kb .. ke - 1.  Tiles are
+    the kernels' 64-key tiles, counted from base = kb - kb % 8.  Whatever the
+    rescale history, the kernels' reference point m never exceeds M(t), the largest
+    score (log2 units) of the keys before tile t, so tile t forces a rescale when
+      kind "sum" (bf16 LDS-DMA kernel: a lane's sum of 32 bf16 P values > 2^11):
+          every key of a full tile scores above M(t) + 6.5 (each P > 2^6.5);
+      kind "max" (E4M3FN and register-staged kernels: tile maximum > m + 8):
+          the tile's maximum is above M(t) + 8.01.
+    Tile 0 only sets m.  Returns the sorted tile indices t >= 1 at which some row
+    forces a rescale; the events hold for any cut of the key range into
+    segments, except at a segment's first tile.
+    """
+    q = np.asarray(q_vals, np.float64)
+    k = np.asarray(k_vals, np.float64)
+    d = q.shape[1]
+    scale = 1.0 / np.sqrt(d) if scale is None else scale
+    s = (q @ k.T) * (scale * LOG2E)
+    base = kb - kb % 8
+    tile = (np.arange(kb, ke) - base) // 64
+    nt = int(tile[-1]) + 1
+    events = []
+    run_max = np.full(q.shape[0], -np.inf)
+    for t in range(nt):
+        cols = np.nonzero(tile == t)[0]
+        st = s[:, cols]
+        full = len(cols) == 64
+        if t > 0:
+            if kind == "sum":
+                hit = full and bool(np.any(st.min(axis=1) > run_max + 6.5))
+            else:
+                hit = bool(np.any(st.max(axis=1) > run_max + 8.01))
+            if hit:
+                events.append(t)
+        run_max = np.maximum(run_max, st.max(axis=1))
+    return events
