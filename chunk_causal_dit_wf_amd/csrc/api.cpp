@@ -32,6 +32,15 @@ wf_status ok() {
   return WF_OK;
 }
 
+}  // namespace
+
+wf_status wf::set_error(wf_status s, const char* msg) {
+  g_err = msg;
+  return s;
+}
+
+namespace {
+
 int esize_of(int32_t dt) {
   switch (dt) {
     case WF_F32: return 4;
@@ -341,7 +350,7 @@ wf_status wf_chunk_attn_workspace_bytes(const wf_kv_cache* c, uint64_t* bytes) {
 // q / o / lse / ws pointers.
 static wf_status plan_attention(const wf_kv_cache* c, int32_t q_dtype, int32_t num_chunks, const int32_t* q_off,
                                 const int64_t* kv_begin, const int64_t* kv_end, float softmax_scale,
-                                uint64_t workspace_bytes, wf::AttnParams& p, wf_attn_plan& L) {
+                                uint64_t workspace_bytes, bool scratch_mode, wf::AttnParams& p, wf_attn_plan& L) {
   wf_status s = check_layout(c);
   if (s != WF_OK) return s;
   if ((s = check_window(c)) != WF_OK) return s;
@@ -437,11 +446,18 @@ static wf_status plan_attention(const wf_kv_cache* c, int32_t q_dtype, int32_t n
   hipError_t e = L.kernel == WF_KERNEL_DMA_BF16 ? wf::attn_dma_resident_blocks(c->head_dim, &resident)
                                                 : wf::attn_fp8_resident_blocks(c->head_dim, &resident);
   if (e != hipSuccess) return fail(WF_ERR_HIP, "device query failed: %s", hipGetErrorString(e));
-  const uint64_t need = (uint64_t)2 * resident * wf::ws_slot_floats(c->head_dim) * sizeof(float);
-  if (workspace_bytes < need)
+  const uint64_t slot_bytes = (uint64_t)wf::ws_slot_floats(c->head_dim) * sizeof(float);
+  const uint64_t need = (uint64_t)2 * resident * slot_bytes;
+  if (!scratch_mode && workspace_bytes < need)
     return fail(WF_ERR_INVALID_ARG, "workspace of %llu bytes is smaller than the %llu required",
                 (unsigned long long)workspace_bytes, (unsigned long long)need);
   if (plan_split(p, (int)items, resident)) {
+    // Slots written: A parts n m, and as many B parts when tails are taken.
+    const uint64_t used = (uint64_t)(p.sp.b > 0 ? 2 : 1) * p.sp.n * p.sp.m * slot_bytes;
+    if (scratch_mode && used > workspace_bytes)
+      return fail(WF_ERR_CAPACITY, "the split schedule of this call needs %llu bytes of scratch; the "
+                  "allocation-free entry point holds %llu", (unsigned long long)used,
+                  (unsigned long long)workspace_bytes);
     L.schedule = WF_SCHED_SPLIT;
     L.parts = p.sp.m;
     L.tail_tiles = p.sp.b;
@@ -457,7 +473,7 @@ wf_status wf_chunk_attn_plan(const wf_kv_cache* c, int32_t q_dtype, int32_t num_
   if (plan == nullptr) return fail(WF_ERR_INVALID_ARG, "plan is NULL");
   wf::AttnParams p;
   wf_attn_plan L;
-  wf_status s = plan_attention(c, q_dtype, num_chunks, q_off, kv_begin, kv_end, 0.f, workspace_bytes, p, L);
+  wf_status s = plan_attention(c, q_dtype, num_chunks, q_off, kv_begin, kv_end, 0.f, workspace_bytes, false, p, L);
   if (s != WF_OK) return s;
   *plan = L;
   return ok();
@@ -467,13 +483,27 @@ wf_status wf_chunk_attn_fwd(const wf_kv_cache* c, const void* q, int32_t q_dtype
                             int32_t num_chunks, const int32_t* q_off, const int64_t* kv_begin,
                             const int64_t* kv_end, float softmax_scale, void* workspace,
                             uint64_t workspace_bytes, void* stream) {
+  return wf::attn_fwd_impl(c, q, q_dtype, o, lse, num_chunks, q_off, kv_begin, kv_end, softmax_scale, workspace,
+                           workspace_bytes, false, stream);
+}
+
+}  // extern "C"
+
+// Attention with a caller workspace (scratch_mode false) or the library's own
+// scratch array (scratch_mode true: the split schedule may use up to
+// workspace_bytes of it; no minimum size is required).
+wf_status wf::attn_fwd_impl(const wf_kv_cache* c, const void* q, int32_t q_dtype, void* o, float* lse,
+                            int32_t num_chunks, const int32_t* q_off, const int64_t* kv_begin,
+                            const int64_t* kv_end, float softmax_scale, void* workspace, uint64_t workspace_bytes,
+                            bool scratch_mode, void* stream) {
   if ((workspace == nullptr) != (workspace_bytes == 0))
     return fail(WF_ERR_INVALID_ARG, "workspace and workspace_bytes must both be set or both be 0");
   if (workspace != nullptr && !aligned(workspace, 256))
     return fail(WF_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   wf::AttnParams p;
   wf_attn_plan L;
-  wf_status s = plan_attention(c, q_dtype, num_chunks, q_off, kv_begin, kv_end, softmax_scale, workspace_bytes, p, L);
+  wf_status s = plan_attention(c, q_dtype, num_chunks, q_off, kv_begin, kv_end, softmax_scale, workspace_bytes,
+                               scratch_mode, p, L);
   if (s != WF_OK) return s;
   const int64_t nq = p.nq;
   if (nq == 0) return ok();
@@ -515,4 +545,4 @@ wf_status wf_chunk_attn_fwd(const wf_kv_cache* c, const void* q, int32_t q_dtype
   return ok();
 }
 
-}  // extern "C"
+

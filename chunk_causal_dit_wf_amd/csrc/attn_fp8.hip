@@ -9,7 +9,12 @@
 // Both products run on V_MFMA_F32_32X32X64_F8F6F4 (e4m3 x e4m3, fp32
 // accumulate), twice the bf16 rate:
 //   S^T = K8 Q8^T: Q is quantised in the kernel, one scale per query row
-//       (sq = amax / 448); the score is acc * ks(key) * sq.
+//       (sq = amax / 448), as two E4M3FN terms: hi = e4m3(q / sq) and
+//       lo = e4m3(q / sq - hi), both multiplied by the same K fragment into
+//       one accumulator.  hi + lo carries q to within 2^-8 |q| + 2^-10 sq
+//       (bf16-like precision), so scores keep the accuracy of a bf16 Q at
+//       the cost of one more fp8 MFMA per 64-dim block.  The score is
+//       acc * ks(key) * sq.
 //   O^T += V8^T P8^T: P is quantised to e4m3 after folding in the V scale,
 //       P'(key) = P(key) * 1.75 * vs(key) / vs_max, where vs_max is the
 //       largest V scale of the block's key range and 1.75 maps the largest
@@ -218,15 +223,17 @@ __device__ __forceinline__ i32x8 v_frag(const char* vbuf, int vx, int db) {
 
 // S^T of one tile in one go (prologue): halves a (keys 0..31) and b (32..63).
 template <int D>
-__device__ __forceinline__ void qk_tile(const char* kbuf, int kx, const i32x8 (&q8)[Geo<D>::KS], f32x16& sa,
-                                        f32x16& sb) {
+__device__ __forceinline__ void qk_tile(const char* kbuf, int kx, const i32x8 (&q8)[Geo<D>::KS],
+                                        const i32x8 (&q8lo)[Geo<D>::KS], f32x16& sa, f32x16& sb) {
   constexpr int KS = Geo<D>::KS;
 #pragma unroll
   for (int i = 0; i < 16; ++i) sa[i] = sb[i] = 0.f;
 #pragma unroll
   for (int i = 0; i < 2 * KS; ++i) {
     f32x16& acc = i < KS ? sa : sb;
-    acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(k_frag<D>(kbuf, kx, i), q8[i % KS], acc, 0, 0, 0, 0, 0, 0);
+    const i32x8 kf = k_frag<D>(kbuf, kx, i);
+    acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf, q8[i % KS], acc, 0, 0, 0, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf, q8lo[i % KS], acc, 0, 0, 0, 0, 0, 0);
   }
 }
 
@@ -345,9 +352,10 @@ __device__ __forceinline__ void segment(const AttnParams& p, const ChunkDesc& cd
     bf.scales[g] = make_float2(e.x, fmaxf(c, cmin));
   }
 
-  // Q row -> e4m3 with one scale per row: lane (lq, hf) holds dims
-  // 64 s + 32 hf + [0, 32) of its row.
-  i32x8 q8[KS];
+  // Q row -> two e4m3 terms with one scale per row: lane (lq, hf) holds dims
+  // 64 s + 32 hf + [0, 32) of its row.  x = q * 448 / amax; hi = e4m3(x);
+  // lo = e4m3(x - hi) (the residual, exact in fp32).
+  i32x8 q8[KS], q8lo[KS];
   float qs;
   {
     const __bf16* qp = (const __bf16*)p.q + ((int64_t)row * p.H + head) * D;
@@ -374,9 +382,16 @@ __device__ __forceinline__ void segment(const AttnParams& p, const ChunkDesc& cd
     for (int s = 0; s < KS; ++s)
 #pragma unroll
       for (int w = 0; w < 8; ++w) {
-        uint32_t v = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(qv[s][w][0] * inv, qv[s][w][1] * inv, 0, false);
-        v = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(qv[s][w][2] * inv, qv[s][w][3] * inv, (int)v, true);
+        const float x0 = qv[s][w][0] * inv, x1 = qv[s][w][1] * inv;
+        const float x2 = qv[s][w][2] * inv, x3 = qv[s][w][3] * inv;
+        uint32_t v = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+        v = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, (int)v, true);
         q8[s][w] = (int)v;
+        const f32x2 h01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(v, 1.0f, false);
+        const f32x2 h23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(v, 1.0f, true);
+        uint32_t u = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x0 - h01[0], x1 - h01[1], 0, false);
+        u = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x2 - h23[0], x3 - h23[1], (int)u, true);
+        q8lo[s][w] = (int)u;
       }
   }
   f32x16 o[DB];
@@ -396,7 +411,7 @@ __device__ __forceinline__ void segment(const AttnParams& p, const ChunkDesc& cd
   }
   // S[0], scaled and masked (tile 0 holds key lo < 8, so its row maxima are finite)
   f32x16 s0a, s0b, s1a, s1b;
-  qk_tile<D>(bf.k0, kx, q8, s0a, s0b);
+  qk_tile<D>(bf.k0, kx, q8, q8lo, s0a, s0b);
   HalfScale h0a = half_scale(bf.scales, 2 * hf, qs), h0b = half_scale(bf.scales, 4 + 2 * hf, qs), h1a, h1b;
   float m = half_max(fmaxf(mask_half(s0a, h0a, 16 * hf, lo, hi), mask_half(s0b, h0b, 32 + 16 * hf, lo, hi)));
   __syncthreads();  // k0 is free for tile 2
@@ -460,6 +475,7 @@ __device__ __forceinline__ void segment(const AttnParams& p, const ChunkDesc& cd
       } else {
         acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fr[i & 1], q8[i % KS], acc, 0, 0, 0, 0, 0, 0);
       }
+      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fr[i & 1], q8lo[i % KS], acc, 0, 0, 0, 0, 0, 0);
       constexpr int e0 = EA * i;
       if constexpr (e0 < 16)
         p_group<e0 % 16, EA>(ca, hca, faa, fab, m, pk, l);

@@ -169,4 +169,13 @@ hipError_t launch_attn_bf16_staged(const AttnParams& p, int head_dim, hipStream_
 hipError_t launch_attn_f32(const AttnParams& p, int head_dim, hipStream_t s);
 hipError_t launch_attn_fp8kv(const AttnParams& p, int head_dim, hipStream_t s);
 
+// Host layer shared by the entry points (api.cpp): the attention call with a
+// caller workspace (scratch_mode false) or with the library's scratch array
+// (scratch_mode true), and the thread-local error text of wf_last_error().
+wf_status attn_fwd_impl(const wf_kv_cache* c, const void* q, int32_t q_dtype, void* o, float* lse,
+                        int32_t num_chunks, const int32_t* q_off, const int64_t* kv_begin, const int64_t* kv_end,
+                        float softmax_scale, void* workspace, uint64_t workspace_bytes, bool scratch_mode,
+                        void* stream);
+wf_status set_error(wf_status s, const char* msg);
+
 }  // namespace wf

@@ -130,25 +130,28 @@ def queries(cfg, layer, rows, std=None, stream=0):
 def staircase(q, k, key_pos, origin, step_keys, rise_log2=16.0, seed_words=(0,)):
     """Peaked-score variant of float32 inputs q [Nq, H, D] and k [L, H, D] (copies are returned).
 
-    Dimension 0 of every query row i is set to a_i and dimension 0 of key j to
-    b_j = c * floor((key_pos[j] - origin) / step_keys), with c chosen so that under
-    the default softmax scale 1/sqrt(D) the product a_i b_j / sqrt(D) rises by
-    rise_log2 * a_i / 8 log2 units (rise_log2 * ln 2 * a_i / 8 nats) per step of
-    step_keys keys.  The row levels a_i are 8 * 2^-L for L = 0..5, or 0 (a flat row):
-    40 % of the rows take the steepest level, the rest spread evenly over the others,
-    so one call mixes flat rows, rows whose last few steps all contribute, and rows
-    dominated by their last step.  Powers of two keep a_i exact in bf16 and, as the
-    largest element of its row, in a per-row E4M3FN quantisation.
+    Dimension 0 of key j is set to b_j = c * floor((key_pos[j] - origin) / step_keys), with c
+    chosen so that a query whose dimension 0 is 8 gains rise_log2 log2 units of score (under the
+    default softmax scale 1/sqrt(D)) per step of step_keys keys.  Every query row gets a level
+    L: 40 % of the rows L = 0, the rest spread evenly over L = 1..5 and "flat".  A row of level L
+    is scaled by 2^-L and its dimension 0 set to 8 * 2^-L, so it climbs rise_log2 * 2^-L per step;
+    a flat row keeps its values and gets dimension 0 = 0.  One call thus mixes flat rows, rows
+    whose last few steps all contribute, and rows dominated by their last step.  Dimension 0 is
+    a power of two and the largest element of its row, so it is exact in bf16 and in a per-row
+    E4M3FN quantisation.
     """
     q = np.array(q, dtype=np.float32, copy=True)
     k = np.array(k, dtype=np.float32, copy=True)
     d = q.shape[-1]
     g = rng(*seed_words)
     lv = g.choice(7, size=q.shape[0], p=[0.4, 0.1, 0.1, 0.1, 0.1, 0.1, 0.1])
-    a = np.where(lv == 6, 0.0, 8.0 * 2.0 ** -lv.astype(np.float64))
+    for L in range(6):
+        rows = lv == L
+        q[rows] *= np.float32(2.0 ** -L)
+        q[rows, :, 0] = np.float32(8.0 * 2.0 ** -L)
+    q[lv == 6, :, 0] = 0.0
     steps = np.floor((np.asarray(key_pos, np.float64) - origin) / step_keys)
     b = steps * rise_log2 * np.log(2.0) * np.sqrt(d) / 8.0
-    q[:, :, 0] = a[:, None]
     k[:, :, 0] = b[:, None]
     return q, k
 

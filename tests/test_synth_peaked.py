@@ -12,10 +12,14 @@ def test_staircase_rises_by_the_stated_log2_units():
     k = synth.normal_f32((1024, 2, 128), 0.5, 99, 2)
     pos = np.arange(1024)
     qs, ks = synth.staircase(q, k, pos, origin=0, step_keys=256, rise_log2=16.0, seed_words=(99, 3))
-    assert np.array_equal(qs[:, :, 1:], q[:, :, 1:]) and np.array_equal(ks[:, :, 1:], k[:, :, 1:])
+    assert np.array_equal(ks[:, :, 1:], k[:, :, 1:])
     a = qs[:, 0, 0].astype(np.float64)
     assert set(np.unique(a)) <= {0.0, 8.0, 4.0, 2.0, 1.0, 0.5, 0.25}
     assert np.mean(a == 8.0) > 0.25
+    for i in range(50):  # a row of level L is the input row times 2^-L; flat rows are unchanged
+        f = a[i] / 8.0 if a[i] > 0 else 1.0
+        assert np.array_equal(qs[i, :, 1:], (q[i, :, 1:] * np.float32(f)).astype(np.float32))
+        assert a[i] == 0 or a[i] >= np.abs(qs[i, :, 1:]).max()   # dimension 0 is the row's largest
     # score offset of dimension 0 under scale 1/sqrt(D), in log2 units: rise * a / 8 per step
     off = np.outer(a, ks[:, 0, 0]) / np.sqrt(128) / np.log(2.0)
     steps = pos // 256
