@@ -78,10 +78,12 @@ def lib():
         L.wf_chunk_attn_fwd.argtypes = [P, vp, i32, vp, vp, i32, ctypes.POINTER(i32), ctypes.POINTER(i64),
                                         ctypes.POINTER(i64), f32, vp, ctypes.c_uint64, vp]
         L.wf_chunk_attn_workspace_bytes.argtypes = [P, ctypes.POINTER(ctypes.c_uint64)]
+        L.wf_chunk_attn_fwd_noalloc.argtypes = [P, vp, i32, vp, vp, i32, ctypes.POINTER(i32), ctypes.POINTER(i64),
+                                                ctypes.POINTER(i64), f32, vp]
         L.wf_chunk_attn_plan.argtypes = [P, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i64), ctypes.POINTER(i64),
                                          ctypes.c_uint64, ctypes.POINTER(wf_attn_plan)]
         for name in ("wf_kv_cache_check", "wf_kv_cache_bytes", "wf_kv_append", "wf_kv_evict", "wf_chunk_attn_fwd",
-                     "wf_chunk_attn_workspace_bytes", "wf_kv_append_quantize", "wf_chunk_attn_plan"):
+                     "wf_chunk_attn_workspace_bytes", "wf_kv_append_quantize", "wf_chunk_attn_plan", "wf_chunk_attn_fwd_noalloc"):
             getattr(L, name).restype = ctypes.c_int
         L.wf_last_error.restype = ctypes.c_char_p
         L.wf_last_error.argtypes = []
@@ -224,6 +226,17 @@ def wf_chunk_attn_fwd(cache, q, q_off, kv_begin, kv_end, softmax_scale=0.0, o=No
     _check(lib().wf_chunk_attn_fwd(ctypes.byref(cache.c), _ptr(q), qd, _ptr(o), _ptr(lse), nc, qo, kb, ke,
                                    float(softmax_scale), _ptr(workspace), wsb, _stream(stream)))
     return (o, lse) if lse is not None else o
+
+
+def wf_chunk_attn_fwd_noalloc(cache, q, q_off, kv_begin, kv_end, o, lse=None, softmax_scale=0.0, stream=None):
+    """wf_chunk_attn_fwd without a workspace and without any allocation: the caller passes o (and lse)."""
+    nc = len(kv_begin)
+    qo = (ctypes.c_int32 * (nc + 1))(*[int(x) for x in q_off])
+    kb = (ctypes.c_int64 * nc)(*[int(x) for x in kv_begin])
+    ke = (ctypes.c_int64 * nc)(*[int(x) for x in kv_end])
+    _check(lib().wf_chunk_attn_fwd_noalloc(ctypes.byref(cache.c), _ptr(q), _q_dtype(q), _ptr(o), _ptr(lse), nc, qo,
+                                           kb, ke, float(softmax_scale), _stream(stream)))
+    return o
 
 
 def _q_dtype(q):

@@ -251,6 +251,25 @@ wf_status wf_chunk_attn_plan(const wf_kv_cache *cache, int32_t q_dtype, int32_t 
  */
 wf_status wf_chunk_attn_workspace_bytes(const wf_kv_cache *cache, uint64_t *bytes);
 
+/*
+ * Allocation-free variant of wf_chunk_attn_fwd, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, results and errors as
+ * wf_chunk_attn_fwd without a workspace argument: where the split schedule
+ * applies, its partial results go to a scratch array inside the library (one
+ * per GPU, WF_NOALLOC_SCRATCH_BYTES, held until the process ends) instead of
+ * a caller workspace.  A call whose split schedule needs more than that is
+ * rejected with WF_ERR_CAPACITY before anything is enqueued.  Calls on one GPU
+ * share its array: calls that may overlap on one GPU (other streams, other
+ * host threads) must be ordered by the caller, or they race.  Nothing is
+ * allocated, freed or synchronised.
+ */
+#define WF_NOALLOC_SCRATCH_BYTES (72u << 20)
+wf_status wf_chunk_attn_fwd_noalloc(const wf_kv_cache *cache, const void *q, int32_t q_dtype, void *o,
+                                    float *lse, int32_t num_chunks, const int32_t *q_off,
+                                    const int64_t *kv_begin, const int64_t *kv_end, float softmax_scale,
+                                    void *stream);
+
 /* Text of the last non-OK status on this thread ("" if none). */
 const char *wf_last_error(void);
 
