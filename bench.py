@@ -79,8 +79,26 @@ def kernel_of(dtype):
 
 
 def source_sha(name):
-    with open(os.path.join(ROOT, "chunk_causal_dit_wf_amd", "csrc", name), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    """sha256 over a kernel source and the local headers it includes (recursively), in include
+    order: a change to any of them invalidates counters taken before it."""
+    csrc = os.path.join(ROOT, "chunk_causal_dit_wf_amd", "csrc")
+    seen, order = set(), []
+
+    def visit(path):
+        path = os.path.normpath(path)
+        if path in seen or not os.path.exists(path):
+            return
+        seen.add(path)
+        order.append(path)
+        for inc in re.findall(r'^#include "([^"]+)"', open(path).read(), re.M):
+            visit(os.path.join(os.path.dirname(path), inc))
+
+    visit(os.path.join(csrc, name))
+    h = hashlib.sha256()
+    for path in order:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def hbm_traffic(kernel, workload, source):

@@ -30,22 +30,50 @@ __device__ __forceinline__ float half_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Work item -> (chunk, query tile, head).  Items are numbered tile-major inside
-// a chunk (item = tile * H + head), so consecutive workgroups -- which the
-// dispatcher spreads round-robin over the 8 XCDs -- visit different heads and
-// each XCD's L2 sees a small, fixed subset of heads.
+// Work item -> (chunk, query tile, head).  The dispatcher deals workgroups
+// round-robin over the 8 XCDs (workgroup g to XCD g % 8), and each XCD has its
+// own L2.  All query tiles of one (chunk, head) read the same keys, so inside
+// a chunk (N = tiles x H items, local index L) the items are dealt so that XCD
+// x = L % 8 takes a contiguous run of the head-major order (head, tile): runs
+// of Q + 1 items for x < R and Q for the rest (N = 8 Q + R); the k-th
+// workgroup of XCD x (k = L / 8) takes position start(x) + k.  Workgroups that
+// run together on one XCD then share one or two heads' keys in its L2.
 struct Item {
   int c, qt, head;
 };
-__device__ __forceinline__ Item decode_item(const AttnParams& p, int item) {
+__device__ __forceinline__ int chunk_of_item(const AttnParams& p, int item) {
   int c = 0;
   while (c + 1 < p.num_chunks && item >= p.chunk[c + 1].item0) ++c;
-  const int local = item - p.chunk[c].item0;
+  return c;
+}
+__device__ __forceinline__ Item decode_item(const AttnParams& p, int item) {
   Item it;
-  it.c = c;
-  it.qt = local / p.H;
-  it.head = local - it.qt * p.H;
+  it.c = chunk_of_item(p, item);
+  const int T = p.chunk[it.c].ntiles;
+  const int N = T * p.H;
+  const int L = item - p.chunk[it.c].item0;
+  const int Q = N >> 3, R = N & 7;
+  const int x = L & 7, k = L >> 3;
+  const int pos = x * Q + min(x, R) + k;
+  it.head = pos / T;
+  it.qt = pos - it.head * T;
   return it;
+}
+// Inverse of decode_item inside chunk c: (query tile, head) -> item.
+__device__ __forceinline__ int encode_item(const AttnParams& p, int c, int qt, int head) {
+  const int T = p.chunk[c].ntiles;
+  const int N = T * p.H;
+  const int Q = N >> 3, R = N & 7;
+  const int pos = head * T + qt;
+  int x, k;
+  if (pos < R * (Q + 1)) {
+    x = pos / (Q + 1);
+    k = pos - x * (Q + 1);
+  } else {
+    x = R + (pos - R * (Q + 1)) / Q;
+    k = pos - R * (Q + 1) - (x - R) * Q;
+  }
+  return p.chunk[c].item0 + 8 * k + x;
 }
 
 constexpr float kRescaleThreshold = 8.0f;  // log2 units: p <= 2^8 between rescales
@@ -156,7 +184,7 @@ __device__ __forceinline__ int part_begin(const SplitSched& sp, int p) { return 
 __device__ __forceinline__ void tile_item(const AttnParams& p, int t, int head, int& c, int& item) {
   c = 0;
   while (c + 1 < p.num_chunks && t * p.H >= p.chunk[c + 1].item0) ++c;
-  item = p.chunk[c].item0 + (t - p.chunk[c].item0 / p.H) * p.H + head;
+  item = encode_item(p, c, t - p.chunk[c].item0 / p.H, head);
 }
 
 // Head-major index of the B part of (item, part p): u = (head * m + p) * tiles + tile.
@@ -185,7 +213,7 @@ __device__ __forceinline__ void walk_segments(const AttnParams& p, int g, Body&&
     if (p.ws == nullptr) {
       item = g;
       j0 = 0;
-      j1 = p.chunk[decode_item(p, g).c].nsteps;
+      j1 = p.chunk[chunk_of_item(p, g)].nsteps;
       slot = -1;
     } else if (g < na) {
       const int part = g / sp.n;
