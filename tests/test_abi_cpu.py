@@ -223,3 +223,30 @@ def test_quantizing_append_validation():
     if not torch.cuda.is_available():
         assert _status(wf.wf_kv_append_quantize, f, 0, k, k) == wf.WF_ERR_HIP
         assert (f.start, f.end) == (0, 0)
+
+
+def test_host_logic_under_address_and_undefined_behavior_sanitizers(tmp_path):
+    """api.cpp built for the host with AddressSanitizer and UndefinedBehaviorSanitizer, linked
+    with host stand-ins of the kernel launchers (tests/sanitize/launch_stubs.cpp), and driven
+    through validation, planning and metadata paths by tests/sanitize/abi_exercise.c.  A
+    sanitizer report aborts the program; every status must match."""
+    san = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined", "-fno-sanitize-recover=all"]
+    hip_host = ["-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include", "-I" + os.path.join(ROOT, "include")]
+    csrc = os.path.join(ROOT, "chunk_causal_dit_wf_amd", "csrc")
+    sdir = os.path.join(ROOT, "tests", "sanitize")
+    steps = [
+        ["g++", "-std=c++17"] + san + hip_host + ["-c", os.path.join(csrc, "api.cpp"), "-o", str(tmp_path / "api.o")],
+        ["g++", "-std=c++17"] + san + hip_host + ["-c", os.path.join(sdir, "launch_stubs.cpp"),
+                                                  "-o", str(tmp_path / "stubs.o")],
+        ["gcc", "-std=c99"] + san + ["-I" + os.path.join(ROOT, "include"), "-c",
+                                     os.path.join(sdir, "abi_exercise.c"), "-o", str(tmp_path / "main.o")],
+        ["g++"] + san + [str(tmp_path / "main.o"), str(tmp_path / "api.o"), str(tmp_path / "stubs.o"),
+                         "-L/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib", "-o", str(tmp_path / "ex")],
+    ]
+    for cmd in steps:
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        assert r.returncode == 0, (cmd, r.stderr[-2000:])
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0", UBSAN_OPTIONS="print_stacktrace=1",
+               HIP_VISIBLE_DEVICES="")
+    r = subprocess.run([str(tmp_path / "ex")], capture_output=True, text=True, env=env, timeout=300)
+    assert r.returncode == 0 and r.stdout.strip().endswith("OK"), (r.stdout[-3000:], r.stderr[-3000:])
