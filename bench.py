@@ -7,10 +7,14 @@ A step is the whole hot path for one new chunk, once per layer:
 Default workload: Wan2.1-1.3B shape, 30 layers, 12 heads x 128, bf16, paged
 ring of 21 pages x 1560 tokens per layer (random page table per layer).
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload round|call|wave|fp8round]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload round|call|wave|fp8round|frameround]
 
 Prints one JSON line.  Inputs are synthetic (seeded on the device) and already
-resident in HBM when the timed region starts.
+resident in HBM when the timed region starts.  The default workload also
+reports, under "extras" (after the headline measurement, which they do not
+change): the same round replayed from captured HIP graphs, the same round on
+peaked scores (the online softmax's re-form path fires), the 14B-shaped fp8
+round, and that round with the quantising append.
 """
 import argparse
 import hashlib
@@ -66,6 +70,13 @@ def parse():
     ap.add_argument("--graph", action="store_true",
                     help="round workloads: after the eager run, replay the round from captured HIP graphs "
                          "(one per ring phase) for the same number of steps and report its rate")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="round workload: skip the extra measurements (graph replay, peaked scores, fp8 round, "
+                         "quantising append)")
+    ap.add_argument("--peaked", action="store_true",
+                    help="round workloads: peaked scores -- dim 0 of every key rises along the chunk "
+                         "(16 log2 units of score per 256 keys against a query dim 0 of 8), so later key tiles "
+                         "outscore earlier ones and the softmax re-forms P with a new maximum")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the timed run, copy a buffer of this many MiB once (a plain copy kernel of "
                          "known size that scales the FETCH_SIZE / WRITE_SIZE counters of a profiled run)")
@@ -121,10 +132,24 @@ def pct(xs, q):
     return ys[min(len(ys) - 1, max(0, int(round(q * (len(ys) - 1)))))]
 
 
+PEAK_Q0 = 8.0              # query dim 0 of the peaked variant
+PEAK_RISE_LOG2 = 16.0      # score rise per PEAK_STEP keys, log2 units
+PEAK_STEP = 256
+
+
+def make_peaked(torch, q, k, D):
+    """Peaked scores: q[:, :, 0] = PEAK_Q0 and k[r, :, 0] rising linearly with the row r of the chunk,
+    PEAK_RISE_LOG2 log2 units of sigma q.k per PEAK_STEP rows (sigma = 1/sqrt(D))."""
+    n = k.shape[0]
+    per_key = PEAK_RISE_LOG2 / PEAK_STEP / (PEAK_Q0 * 1.4426950408889634 / D ** 0.5)
+    q[:, :, 0] = PEAK_Q0
+    k[:, :, 0] = (torch.arange(n, device=k.device, dtype=torch.float32) * per_key)[:, None].to(k.dtype)
+
+
 class Layer:
     """One layer's cache plus the device inputs of its chunk."""
 
-    def __init__(self, wf, torch, synth, cfg, layer, gen, bf16_source=False):
+    def __init__(self, wf, torch, synth, cfg, layer, gen, bf16_source=False, peaked=False):
         H, D, dt = cfg["H"], cfg["D"], cfg["dtype"]
         n = cfg.get("chunk", CHUNK)
         table = synth.permuted_table(synth.W_WAN_ROUND if dt == "bf16" else synth.W_14B_FP8, layer, 21)
@@ -136,6 +161,8 @@ class Layer:
             self.k = (torch.randn((n, H, D), generator=gen, device="cuda") * std).to(torch.bfloat16)
             self.v = (torch.randn((n, H, D), generator=gen, device="cuda") * std).to(torch.bfloat16)
             self.ks = self.vs = None
+            if peaked:
+                make_peaked(torch, self.q, self.k, D)
         else:
             self.k, self.ks = quantize_dev(torch, torch.randn((n, H, D), generator=gen, device="cuda") * std)
             self.v, self.vs = quantize_dev(torch, torch.randn((n, H, D), generator=gen, device="cuda") * std)
@@ -170,7 +197,8 @@ def run_round(args, cfg):
     gen = torch.Generator(device="cuda")
     gen.manual_seed(synth.SEED)
     quant = cfg["dtype"] == "fp8" and getattr(args, "quantize_append", False)
-    layers = [Layer(wf, torch, synth, cfg, l, gen, bf16_source=quant) for l in range(cfg["layers"])]
+    peaked = cfg["dtype"] == "bf16" and getattr(args, "peaked", False)
+    layers = [Layer(wf, torch, synth, cfg, l, gen, bf16_source=quant, peaked=peaked) for l in range(cfg["layers"])]
 
     def append(L, pos):
         if quant:
@@ -256,9 +284,12 @@ def run_round(args, cfg):
         g1.record()
         torch.cuda.synchronize()
         gms = g0.elapsed_time(g1) / args.steps
-        graph = dict(graph_ms_per_step=round(gms, 4), graph_chunks_per_s=round(1000.0 / gms, 3),
-                     graph_tflops=round(flops_per_launch * cfg["layers"] / (gms * 1e-3) / 1e12, 2),
-                     graph_phases=rr.period)
+        graph = dict(ms_per_step=round(gms, 4), chunks_per_s=round(1000.0 / gms, 3),
+                     tflops=round(flops_per_launch * cfg["layers"] / (gms * 1e-3) / 1e12, 2),
+                     phases=rr.period, steps=args.steps)
+    del layers
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
     return dict(
         plan=plan, graph=graph,
         ms_per_step=ms_step, wall_s=wall, value=total_flops / (total_ms * 1e-3) / 1e12,
@@ -343,6 +374,47 @@ def cpu_baseline(rows, H, D, keys):
                        % (rows, keys, H, D, dt))
 
 
+def extras(args):
+    """Extra measurements of the default run (each a short run of its own after the headline)."""
+    import copy
+    import torch
+    out = {}
+
+    def sub_args(**kw):
+        a = copy.copy(args)
+        a.graph = a.peaked = a.quantize_append = False
+        a.steps, a.warmup = kw.pop("steps", 5), kw.pop("warmup", 2)
+        for k, v in kw.items():
+            setattr(a, k, v)
+        return a
+
+    def summary(r, peak):
+        d = dict(value=round(r["value"], 3), unit="TFLOP/s", ms_per_step=round(r["ms_per_step"], 4),
+                 chunks_per_s=round(r["chunks_per_s"], 3), attn_kernel_tflops=round(r["attn_tflops"], 2),
+                 attn_frac_of_peak=round(r["attn_tflops"] / peak, 4), kv_append_GBps=round(r["append_gbps"], 1),
+                 schedule=r["plan"]["schedule"], attn_grid=r["plan"]["grid"])
+        return d
+
+    r = run_round(sub_args(steps=args.steps, warmup=args.warmup, graph=True), WORKLOADS["round"])
+    out["graph_replay"] = dict(r["graph"], workload="the headline round replayed from one captured HIP graph "
+                                                    "per ring phase (evict metadata on the host)")
+    r = run_round(sub_args(peaked=True), WORKLOADS["round"])
+    out["peaked"] = dict(summary(r, BF16_PEAK_TFLOPS), workload="the headline round on peaked scores: "
+                         "query dim 0 = %g, key dim 0 rising %g log2 units of score per %d keys" %
+                         (PEAK_Q0, PEAK_RISE_LOG2, PEAK_STEP), steps=5)
+    r = run_round(sub_args(steps=3, warmup=1), WORKLOADS["fp8round"])
+    out["fp8round"] = dict(summary(r, FP8_PEAK_TFLOPS), workload=WORKLOADS["fp8round"]["name"], steps=3,
+                           append_bytes_per_launch=r["append_bytes"])
+    r = run_round(sub_args(steps=3, warmup=1, quantize_append=True), WORKLOADS["fp8round"])
+    out["quantize_append"] = dict(
+        kv_append_GBps=round(r["append_gbps"], 1), append_kernel_ms=round(r["append_kernel_ms"], 5),
+        append_frac_of_hbm=round(r["append_gbps"] / HBM_PEAK_GBPS, 4), bytes_per_launch=r["append_bytes"],
+        chunks_per_s=round(r["chunks_per_s"], 3), steps=3,
+        workload="the 14B fp8 round with bf16 K/V quantised to E4M3FN by the append (quant_append_kernel)")
+    torch.cuda.synchronize()
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -377,7 +449,8 @@ def main():
         "dtype": "bf16" if cfg["dtype"] == "bf16" else "e4m3 (fp8 MFMA; bf16 Q and P quantised in-kernel, e4m3 K,V)",
         "append_mode": ("quantising bf16 -> e4m3" if getattr(args, "quantize_append", False) and cfg["dtype"] == "fp8"
                         else "copy"),
-        "data": "synthetic (seeded N(0, s^2) on device, random page tables)",
+        "data": ("synthetic (seeded N(0, s^2) on device, random page tables%s)" %
+                 (", peaked scores" if args.peaked else "")),
         "config": {"workload": cfg["name"], "layers": cfg["layers"], "heads": r["H"], "head_dim": r["D"],
                    "query_rows": cfg.get("chunk", CHUNK), "keys": WINDOW if "round" in args.workload else None,
                    "parallelism": "single GPU", "schedule": r["plan"]["schedule"],
@@ -405,6 +478,8 @@ def main():
                                   "bytes_per_launch": r["append_bytes"]}
     if r.get("graph"):
         out["graph_replay"] = r["graph"]
+    if args.workload == "round" and not args.no_extras and not args.peaked:
+        out["extras"] = extras(args)
     if args.calib_copy_mib > 0:
         calib_copy(args.calib_copy_mib)
     if not args.no_cpu_baseline:

@@ -943,8 +943,8 @@ __device__ __forceinline__ void segment(const AttnParams& p, const ChunkDesc& cd
   // so that every slot is a compile-time constant (the compiler can then tell
   // the LDS-DMA targets from the buffers being read); every call site below
   // has a static ring position.  steady(t) needs t + 2 < nt: S(t+1) needs no
-  // mask and V tile t+1 no zeroing.  edge_step(t) is tile nt - 2, last() tile
-  // nt - 1.
+  // mask and V tile t+1 no zeroing.  edge_step(t) is tile nt - 2; tile nt - 1
+  // follows the switch.
   auto steady = [&](auto rho_tag, int t) {
     constexpr int rho = decltype(rho_tag)::value;
     constexpr int sl = (rho + 1) % 3;
@@ -967,11 +967,6 @@ __device__ __forceinline__ void segment(const AttnParams& p, const ChunkDesc& cd
     end_phase();
     if (group == 0 && ze) zero_v(rg.v<sn>(), t + 1);
   };
-  auto last = [&](auto rho_tag) {
-    constexpr int sl = (decltype(rho_tag)::value + 1) % 3;
-    m_phase<D, false, true>(s, o, qf, pf, rg.k<sl>(), rg.v<sl>(), kx, vx);
-    end_phase();
-  };
   int t = 0;
   for (; t + 4 < nt; t += 3) {
     steady(IC<0>{}, t);
@@ -980,23 +975,30 @@ __device__ __forceinline__ void segment(const AttnParams& p, const ChunkDesc& cd
   }
   switch (nt - t) {  // 1 .. 4 tiles left, t % 3 == 0
     case 1:
-      last(IC<0>{});
       break;
     case 2:
       edge_step(IC<0>{}, t);
-      last(IC<1>{});
       break;
     case 3:
       steady(IC<0>{}, t);
       edge_step(IC<1>{}, t + 1);
-      last(IC<2>{});
       break;
     default:
       steady(IC<0>{}, t);
       steady(IC<1>{}, t + 1);
       edge_step(IC<2>{}, t + 2);
-      last(IC<0>{});
       break;
+  }
+  // Tile nt - 1: its P V product alone, from slot nt % 3 (one code path for
+  // every tile count).  The epilogue reads the accumulators with plain VALU
+  // code right after, so the wave first sleeps until the products have left
+  // the matrix pipe.
+  {
+    const int sl = nt % 3;
+    const char* vt = sl == 0 ? rg.v0 : sl == 1 ? rg.v1 : rg.v2;
+    m_phase<D, false, true>(s, o, qf, pf, rg.k0, vt, kx, vx);
+    __builtin_amdgcn_s_sleep(2);
+    end_phase();
   }
   if (group == 0) barrier();  // matches group 1's last M phase
 
