@@ -255,6 +255,26 @@ __device__ __forceinline__ void static_for(F&& f) {
   static_for_seq(f, std::make_integer_sequence<int, N>{});
 }
 
+// Per-key factors of the 8-key groups a lane holds in one tile: group
+// 4 h + 2 hf + j (half h, j = 0, 1).  tab[g] = (ks, c, 2^-c, 0): K scale, V
+// bias c = log2(1.75 vs / vs_max) and its weight for the row sum.
+struct Factors {
+  float f[4], c[4], w[4];  // index 2 h + j
+};
+__device__ __forceinline__ Factors factors(const float4* tab, int t, int hf, float qs) {
+  Factors F;
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const float4 e = tab[8 * t + 4 * h + 2 * hf + j];
+      F.f[2 * h + j] = e.x * qs;
+      F.c[2 * h + j] = e.y;
+      F.w[2 * h + j] = e.z;
+    }
+  return F;
+}
+
 // Phase M of one 64-key tile.  QK: S(t+1) = K(t+1) (Qhi + Qlo)^T from the K
 // tile at kt into s[0] (keys 0..31) and s[1] (32..63).  PV: O^T += V(t)^T
 // P'(t) from the V^T tile at vt.  Order per k-block kb: the hi products of
@@ -262,14 +282,55 @@ __device__ __forceinline__ void static_for(F&& f) {
 // 2 kb + 1 (D / 32 = 2 D / 64 PV products in all).  Each accumulator's
 // products are at least two MFMAs apart.  Every index is a compile-time
 // constant.
-template <int D, bool QK, bool PV>
+//
+// XPRE (steady tiles, both products): every Q K^T product first, then the
+// P V products, then -- while those run on the matrix pipe -- the first step
+// of the softmax, x = S f_q + c_q - m, in place in s (F: the factors of the
+// tile of S, m: the current reference point).  This moves a quarter of the
+// softmax's vector work from phase V, which is the longer one, into phase M.
+template <int D, bool QK, bool PV, bool XPRE = false>
 __device__ __forceinline__ void m_phase(f32x16 (&s)[2], f32x16 (&o)[D / 32], const i32x8 (&qh)[D / 64],
                                         const i32x8 (&ql)[D / 64], const i32x8& p8, const char* kt,
-                                        const char* vt, int kx, int vx) {
+                                        const char* vt, int kx, int vx, const Factors* F = nullptr,
+                                        float m = 0.f) {
   constexpr int KS = D / 64;
   constexpr int DB = D / 32;
   static_assert(DB == 2 * KS, "two PV products per k-block");
-  if constexpr (QK) {
+  static_assert(!XPRE || (QK && PV), "XPRE needs both products");
+  if constexpr (XPRE) {
+    i32x8 fa = k_frag<D>(kt, kx, 0, 0), fb = k_frag<D>(kt, kx, 1, 0);
+    static_for<KS>([&](auto KB) {
+      constexpr int kb = decltype(KB)::value;
+      if constexpr (kb == 0) {
+        s[0] = mfma8z(fa, qh[0]);
+        s[1] = mfma8z(fb, qh[0]);
+      } else {
+        s[0] = mfma8(fa, qh[kb], s[0]);
+        s[1] = mfma8(fb, qh[kb], s[1]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      s[0] = mfma8(fa, ql[kb], s[0]);
+      if constexpr (kb + 1 < KS) fa = k_frag<D>(kt, kx, 0, kb + 1);
+      s[1] = mfma8(fb, ql[kb], s[1]);
+      if constexpr (kb + 1 < KS) fb = k_frag<D>(kt, kx, 1, kb + 1);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    i32x8 fv = v_frag<D>(vt, vx, 0);
+    static_for<DB>([&](auto DBI) {
+      constexpr int db = decltype(DBI)::value;
+      const i32x8 f = fv;
+      if constexpr (db + 1 < DB) fv = v_frag<D>(vt, vx, db + 1);
+      o[db] = mfma8(f, p8, o[db]);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    float cm[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) cm[q] = F->c[q] - m;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[h][e] = __builtin_fmaf(s[h][e], F->f[2 * h + e / 8], cm[2 * h + e / 8]);
+  } else if constexpr (QK) {
     i32x8 fa = k_frag<D>(kt, kx, 0, 0), fb = k_frag<D>(kt, kx, 1, 0);
     i32x8 fv;
     if constexpr (PV) fv = v_frag<D>(vt, vx, 0);
@@ -320,26 +381,6 @@ __device__ __forceinline__ void m_phase(f32x16 (&s)[2], f32x16 (&o)[D / 32], con
   }
 }
 
-// Per-key factors of the 8-key groups a lane holds in one tile: group
-// 4 h + 2 hf + j (half h, j = 0, 1).  tab[g] = (ks, c, 2^-c, 0): K scale, V
-// bias c = log2(1.75 vs / vs_max) and its weight for the row sum.
-struct Factors {
-  float f[4], c[4], w[4];  // index 2 h + j
-};
-__device__ __forceinline__ Factors factors(const float4* tab, int t, int hf, float qs) {
-  Factors F;
-#pragma unroll
-  for (int h = 0; h < 2; ++h)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const float4 e = tab[8 * t + 4 * h + 2 * hf + j];
-      F.f[2 * h + j] = e.x * qs;
-      F.c[2 * h + j] = e.y;
-      F.w[2 * h + j] = e.z;
-    }
-  return F;
-}
-
 // Phase V: P'(t+1) from the raw products S(t+1) (both 32-key halves, 32
 // elements per lane; element e of half h is key kb + 32 h + 16 hf + e of the
 // segment, scale group q = 2 h + e / 8):
@@ -350,9 +391,11 @@ __device__ __forceinline__ Factors factors(const float4* tab, int t, int hf, flo
 // element could then exceed e4m3's range): then the row maximum is taken, O
 // and l are rescaled exactly, x is shifted by the move and P' formed again.
 // FIRST: the first tile of a segment sets m from its own row maxima.
-template <int D, bool MASK, bool FIRST>
+// XPRE: s already holds x (computed in phase M; no mask, not the first tile).
+template <int D, bool MASK, bool FIRST, bool XPRE = false>
 __device__ __forceinline__ void v_phase(f32x16 (&s)[2], i32x8& p8, f32x16 (&o)[D / 32], float& m, float& l,
                                         const Factors& F, int kb, int lo, int hi, int hf) {
+  static_assert(!XPRE || (!MASK && !FIRST), "x is formed in phase M only for unmasked, later tiles");
   // Key of element e of half h, from an opaque copy of hf (per-element key
   // offsets would otherwise be precomputed once and held in registers).
   int k0 = kb + 16 * hf;
@@ -375,7 +418,7 @@ __device__ __forceinline__ void v_phase(f32x16 (&s)[2], i32x8& p8, f32x16 (&o)[D
     m = half_max(a);
     l = 0.f;
   }
-  {
+  if constexpr (!XPRE) {
     float cm[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) cm[q] = F.c[q] - m;
@@ -621,10 +664,11 @@ __device__ __forceinline__ void segment(const AttnParams& p, const ChunkDesc& cd
   auto steady = [&](auto rho_tag, int t) {
     constexpr int rho = decltype(rho_tag)::value;
     constexpr int sl = (rho + 1) % 3;
-    m_phase<D, true, true>(s, o, qh, ql, p8, rg.k<sl>(), rg.v<sl>(), kx, vx);
+    const Factors F = factors(rg.tab, t + 1, hf, qs);
+    m_phase<D, true, true, true>(s, o, qh, ql, p8, rg.k<sl>(), rg.v<sl>(), kx, vx, &F, m);
     end_phase();
     loads(t, rg.v<rho>(), rg.k<sl>());
-    v_phase<D, false, false>(s, p8, o, m, l, factors(rg.tab, t + 1, hf, qs), 0, lo, hi, hf);
+    v_phase<D, false, false, true>(s, p8, o, m, l, factors(rg.tab, t + 1, hf, qs), 0, lo, hi, hf);
     end_phase();
   };
   auto edge_step = [&](auto rho_tag, int t) {
