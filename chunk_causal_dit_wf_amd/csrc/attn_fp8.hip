@@ -315,21 +315,24 @@ __device__ __forceinline__ void m_phase(f32x16 (&s)[2], f32x16 (&o)[D / 32], con
       if constexpr (kb + 1 < KS) fb = k_frag<D>(kt, kx, 1, kb + 1);
       __builtin_amdgcn_sched_barrier(0);
     });
+    float cm[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) cm[q] = F->c[q] - m;
+    // Each P V product is followed by the x of 32 / DB elements of S.
+    constexpr int PER = 32 / DB;
     i32x8 fv = v_frag<D>(vt, vx, 0);
     static_for<DB>([&](auto DBI) {
       constexpr int db = decltype(DBI)::value;
       const i32x8 f = fv;
       if constexpr (db + 1 < DB) fv = v_frag<D>(vt, vx, db + 1);
       o[db] = mfma8(f, p8, o[db]);
+      static_for<PER>([&](auto I) {
+        constexpr int i = PER * db + decltype(I)::value;
+        constexpr int h = i / 16, e = i % 16;
+        s[h][e] = __builtin_fmaf(s[h][e], F->f[2 * h + e / 8], cm[2 * h + e / 8]);
+      });
       __builtin_amdgcn_sched_barrier(0);
     });
-    float cm[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) cm[q] = F->c[q] - m;
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) s[h][e] = __builtin_fmaf(s[h][e], F->f[2 * h + e / 8], cm[2 * h + e / 8]);
   } else if constexpr (QK) {
     i32x8 fa = k_frag<D>(kt, kx, 0, 0), fb = k_frag<D>(kt, kx, 1, 0);
     i32x8 fv;
