@@ -352,6 +352,34 @@ def calib_copy(mib):
     del x, y
 
 
+def copy_calibration(nbytes, nbuf=30, reps=3):
+    """Achievable rate of a plain device copy moving the append's bytes (read nbytes, write nbytes),
+    over nbuf distinct source/destination pairs (the rounds' per-layer rotation, so no copy is served
+    from the previous one's lines in the 256 MB MALL): the practical HBM ceiling for a single
+    kernel of the append's size, launch and ramp included."""
+    import torch
+    src = [torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(i) for i in range(nbuf)]
+    dst = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(nbuf)]
+    for a, b in zip(src, dst):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    ms = []
+    for _ in range(reps):
+        for a, b in zip(src, dst):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            b.copy_(a)
+            e1.record()
+            ms.append((e0, e1))
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) for a, b in ms)
+    med = t[len(t) // 2]
+    del src, dst
+    torch.cuda.empty_cache()
+    return dict(GBps=round(2 * nbytes / (med * 1e-3) / 1e9, 1), ms=round(med, 5), bytes_per_copy=2 * nbytes,
+                copies=len(t), kernel="torch copy_ (a plain device copy kernel)")
+
+
 def cpu_baseline(rows, H, D, keys):
     """Time the float64 oracle on the host for one layer's attention (rows x keys x H)."""
     import numpy as np
@@ -476,6 +504,10 @@ def main():
                                   "kernel": ("quant_append_kernel<128>" if out["append_mode"] != "copy" else
                                              "append_kernel<%d, 128>" % (2 if cfg["dtype"] == "bf16" else 1)),
                                   "bytes_per_launch": r["append_bytes"]}
+        if not args.no_extras:
+            cal = copy_calibration(r["append_bytes"] // 2)
+            cal["append_frac_of_copy"] = round(r["append_gbps"] / cal["GBps"], 4)
+            out["append_roofline"]["copy_calibration"] = cal
     if r.get("graph"):
         out["graph_replay"] = r["graph"]
     if args.workload == "round" and not args.no_extras and not args.peaked:

@@ -672,13 +672,31 @@ __device__ __forceinline__ void zero_v_outside(char* vt, int t, int lo, int hi) 
   }
 }
 
+// Row sums on the matrix unit.  A 16x16x32 bf16 product reads a P fragment
+// of the 32x32x16 P V product as its B operand: lane L holds keys
+// 8 (L / 32) + j of query L % 32, which that product takes as k = 8 (L / 16) + j
+// of column L % 16.  With the selector A = rows 0 and 1 of ones over the
+// k-blocks of queries L % 16 and L % 16 + 16 (lanes 0, 32 and 17, 49), output
+// row 0 / row 1 of column n is the sum of P over the fragment's 16 keys for
+// query n / n + 16: lanes 0..15 accumulate l in lacc[0] (query L) and lacc[1]
+// (query L + 16), summed from the same bf16 P the P V product multiplies.
+__device__ __forceinline__ bf16x8 row_sum_selector(int lane) {
+  const bool one = lane == 0 || lane == 32 || lane == 17 || lane == 49;
+  bf16x8 a;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) a[j] = one ? (__bf16)1.0f : (__bf16)0.0f;
+  return a;
+}
+
 // Phase M of one 64-key tile.  QK: S(t+1) = K(t+1) Q^T from the K tile at kt
-// (two halves into s[0], s[1]).  PV: O^T += V(t)^T P(t) from the V tile at vt.
+// (two halves into s[0], s[1]).  PV: O^T += V(t)^T P(t) from the V tile at vt,
+// and lacc += the row sums of P(t) (one 16x16x32 product per P fragment).
 // kx / vx: this lane's LDS byte offsets of its K row chunk and of its V^T row
 // chunk.  Fragment reads run DIST products ahead of their use.
 template <int D, bool QK, bool PV>
 __device__ __forceinline__ void m_phase(f32x16 (&s)[2], f32x16 (&o)[D / 32], const bf16x8 (&qf)[D / 16],
-                                        const bf16x8 (&pf)[4], const char* kt, const char* vt, int kx, int vx) {
+                                        const bf16x8 (&pf)[4], const char* kt, const char* vt, int kx, int vx,
+                                        const bf16x8& sel, f32x4& lacc) {
   using G = Geo<D>;
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
@@ -716,6 +734,7 @@ __device__ __forceinline__ void m_phase(f32x16 (&s)[2], f32x16 (&o)[D / 32], con
     } else {
       const int j = 2 * ks + (r - (QK ? 2 : 0));
       o[j % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, pf[j / DB], o[j % DB], 0, 0, 0);
+      if (j % DB == DB - 1) lacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, pf[j / DB], lacc, 0, 0, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -725,26 +744,27 @@ __device__ __forceinline__ void m_phase(f32x16 (&s)[2], f32x16 (&o)[D / 32], con
   if constexpr (PV) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) asm volatile("" : "+v"(o[db]));
+    asm volatile("" : "+v"(lacc));
   }
 }
 
 // Phase V: softmax of S(t+1) (both 32-key halves, 32 elements per lane).
 //
 // The reference point m of the online softmax is moved only when needed: P is
-// formed with the current m, and only if some lane's partial row sum exceeds
-// 2^11 (so some p > 2^6, i.e. a score more than 6 above m) is the row
-// maximum taken and O, l rescaled exactly before P is formed again.  Every
-// p stays below 2^12 (no overflow; bf16 keeps its relative precision), and
-// the common path needs no maximum.  FIRST: the first tile of a segment sets
-// m from its own row maxima.  MASK: keys outside [lo, hi) (tile-relative key
-// kb + ...) are set to -inf first.  The wave runs this phase alone on its
-// SIMD's vector unit, so each step is applied to all 32 elements before the
-// next: independent instructions cover each other's latency.
+// formed with the current m, x = S sl2 - m, and only if some x exceeds 11 (a
+// p above 2^11) is the row maximum taken and O and the row sums rescaled
+// exactly before P is formed again.  Every p stays at most 2^11 (no overflow;
+// bf16 keeps its relative precision), and the common path needs no exact
+// maximum: the guard is a max3 tree over x, which does not wait for the
+// exponentials.  The row sums themselves are taken on the matrix unit in phase
+// M (row_sum_selector).  FIRST: the first tile of a segment sets m from its own
+// row maxima.  MASK: keys outside [lo, hi) (tile-relative key kb + ...) are
+// set to -inf first.  Each step is applied to all 32 elements before the next:
+// independent instructions cover each other's latency.
 template <int D, bool MASK, bool FIRST>
 __device__ __forceinline__ void v_phase(f32x16 (&s)[2], bf16x8 (&pf)[4], f32x16 (&o)[D / 32], float& m,
-                                        float& l, float sl2, int kb, int lo, int hi, int hf) {
+                                        f32x4& lacc, float sl2, int kb, int lo, int hi, int hf) {
   typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
-  const bf16x2v ones = {(__bf16)1.0f, (__bf16)1.0f};
   if constexpr (MASK) {
 #pragma unroll
     for (int h = 0; h < 2; ++h)
@@ -766,7 +786,7 @@ __device__ __forceinline__ void v_phase(f32x16 (&s)[2], bf16x8 (&pf)[4], f32x16 
     }
     return half_max(fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]))) * sl2;
   };
-  // P = exp2(S sl2 - m) into pf; returns this lane's sum of the bf16 values.
+  // P = exp2(x), x = S sl2 - m, into pf; returns this lane's largest x.
   auto form_p = [&]() {
     const float nm = -m;
     float e[2][16];
@@ -775,12 +795,14 @@ __device__ __forceinline__ void v_phase(f32x16 (&s)[2], bf16x8 (&pf)[4], f32x16 
 #pragma unroll
       for (int k = 0; k < 16; ++k) e[h][k] = __builtin_fmaf(s[h][k], sl2, nm);
     __builtin_amdgcn_sched_barrier(0);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 32; i += 2) mx = fmaxf(fmaxf(e[i >> 4][i & 15], e[i >> 4][(i & 15) + 1]), mx);
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int k = 0; k < 16; ++k) e[h][k] = __builtin_amdgcn_exp2f(e[h][k]);
     __builtin_amdgcn_sched_barrier(0);
-    float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -788,30 +810,28 @@ __device__ __forceinline__ void v_phase(f32x16 (&s)[2], bf16x8 (&pf)[4], f32x16 
         const bf16x2v pk = {(__bf16)e[h][k], (__bf16)e[h][k + 1]};
         pf[2 * h + (k >> 3)][k & 7] = pk[0];
         pf[2 * h + (k >> 3)][(k & 7) + 1] = pk[1];
-        ls[(k >> 1) & 3] = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, ls[(k >> 1) & 3], false);
       }
-    return (ls[0] + ls[1]) + (ls[2] + ls[3]);
+    return mx;
   };
-  if constexpr (FIRST) {
-    m = row_max();
-    l = 0.f;
-  }
-  float lsum = form_p();
-  if (!FIRST && __builtin_expect(__builtin_amdgcn_ballot_w64(!(lsum <= 2048.f)) != 0, 0)) {
+  if constexpr (FIRST) m = row_max();
+  const float mx = form_p();
+  if (!FIRST && __builtin_expect(__builtin_amdgcn_ballot_w64(!(mx <= 11.f)) != 0, 0)) {
     asm volatile("");  // a real branch: the recomputation must not be executed speculatively
     const float m_new = fmaxf(m, row_max());
     const float alpha = __builtin_amdgcn_exp2f(m - m_new);
     m = m_new;
-    l *= alpha;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
-    lsum = form_p();
+    // lacc[0] of lane L < 16 is relative to row L's m, lacc[1] to row L + 16's.
+    const float alpha_hi = __shfl_down(alpha, 16);
+    lacc[0] *= alpha;
+    lacc[1] *= alpha_hi;
+    form_p();
   }
-  l += lsum;
   // Keep the softmax in this phase.
-  asm volatile("" : "+v"(pf[0]), "+v"(pf[1]), "+v"(pf[2]), "+v"(pf[3]), "+v"(l));
+  asm volatile("" : "+v"(pf[0]), "+v"(pf[1]), "+v"(pf[2]), "+v"(pf[3]), "+v"(lacc));
 }
 
 // LDS stages: K tile and V^T tile of each of the three ring slots, as
@@ -885,7 +905,9 @@ __device__ __forceinline__ void segment(const AttnParams& p, const ChunkDesc& cd
     for (int i = 0; i < 16; ++i) o[b][i] = 0.f;
   f32x16 s[2];
   bf16x8 pf[4];
-  float m = -INFINITY, l = 0.f;
+  float m = -INFINITY;
+  f32x4 lacc = {0.f, 0.f, 0.f, 0.f};
+  const bf16x8 sel = row_sum_selector(lane);
 
   auto end_phase = [&]() {
     if (pend)
@@ -930,12 +952,12 @@ __device__ __forceinline__ void segment(const AttnParams& p, const ChunkDesc& cd
   barrier();
   if (group == 1) barrier();  // group 1 runs one phase behind
   // M(-1): S(0) from K(0) in slot 0.
-  m_phase<D, true, false>(s, o, qf, pf, rg.k<0>(), rg.v<0>(), kx, vx);
+  m_phase<D, true, false>(s, o, qf, pf, rg.k<0>(), rg.v<0>(), kx, vx, sel, lacc);
   end_phase();
   if (group == 1 && vedge(0)) zero_v(rg.v<1>(), 0);
   // V(-1)
   loads(-1, rg.v<2>(), rg.k<0>());
-  v_phase<D, true, true>(s, pf, o, m, l, sl2, 0, lo, hi, hf);
+  v_phase<D, true, true>(s, pf, o, m, lacc, sl2, 0, lo, hi, hf);
   end_phase();
   if (group == 0 && vedge(0)) zero_v(rg.v<1>(), 0);
 
@@ -948,22 +970,22 @@ __device__ __forceinline__ void segment(const AttnParams& p, const ChunkDesc& cd
   auto steady = [&](auto rho_tag, int t) {
     constexpr int rho = decltype(rho_tag)::value;
     constexpr int sl = (rho + 1) % 3;
-    m_phase<D, true, true>(s, o, qf, pf, rg.k<sl>(), rg.v<sl>(), kx, vx);
+    m_phase<D, true, true>(s, o, qf, pf, rg.k<sl>(), rg.v<sl>(), kx, vx, sel, lacc);
     end_phase();
     loads(t, rg.v<rho>(), rg.k<sl>());
-    v_phase<D, false, false>(s, pf, o, m, l, sl2, 0, lo, hi, hf);
+    v_phase<D, false, false>(s, pf, o, m, lacc, sl2, 0, lo, hi, hf);
     end_phase();
   };
   auto edge_step = [&](auto rho_tag, int t) {
     constexpr int rho = decltype(rho_tag)::value;
     constexpr int sl = (rho + 1) % 3;
     constexpr int sn = (rho + 2) % 3;  // slot of stage t + 1
-    m_phase<D, true, true>(s, o, qf, pf, rg.k<sl>(), rg.v<sl>(), kx, vx);
+    m_phase<D, true, true>(s, o, qf, pf, rg.k<sl>(), rg.v<sl>(), kx, vx, sel, lacc);
     end_phase();
     const bool ze = vedge(t + 1);
     if (group == 1 && ze) zero_v(rg.v<sn>(), t + 1);
     loads(t, rg.v<rho>(), rg.k<sl>());
-    v_phase<D, true, false>(s, pf, o, m, l, sl2, BN * (t + 1), lo, hi, hf);
+    v_phase<D, true, false>(s, pf, o, m, lacc, sl2, BN * (t + 1), lo, hi, hf);
     end_phase();
     if (group == 0 && ze) zero_v(rg.v<sn>(), t + 1);
   };
@@ -996,13 +1018,15 @@ __device__ __forceinline__ void segment(const AttnParams& p, const ChunkDesc& cd
   {
     const int sl = nt % 3;
     const char* vt = sl == 0 ? rg.v0 : sl == 1 ? rg.v1 : rg.v2;
-    m_phase<D, false, true>(s, o, qf, pf, rg.k0, vt, kx, vx);
+    m_phase<D, false, true>(s, o, qf, pf, rg.k0, vt, kx, vx, sel, lacc);
     __builtin_amdgcn_s_sleep(2);
     end_phase();
   }
   if (group == 0) barrier();  // matches group 1's last M phase
 
-  const float lt = half_sum(l);
+  // Row sum of row lq: lacc[lq / 16] of lane lq % 16.
+  const float l_lo = __shfl(lacc[0], lq & 15), l_hi = __shfl(lacc[1], lq & 15);
+  const float lt = lq < 16 ? l_lo : l_hi;
   if (slot < 0) {
     const float inv = 1.f / lt;
     if (row_ok) {

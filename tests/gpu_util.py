@@ -114,14 +114,16 @@ def rescale_events(q_vals, k_vals, kb, ke, kind, scale=None):
     the kernels' 64-key tiles, counted from base = kb - kb % 8.  Whatever the
     rescale history, the kernels' reference point m never exceeds M(t), the largest
     score (log2 units) of the keys before tile t, so tile t forces a rescale when
-      kind "sum" (bf16 LDS-DMA kernel: a lane's sum of 32 bf16 P values > 2^11):
-          every key of a full tile scores above M(t) + 6.5 (each P > 2^6.5);
-      kind "max" (E4M3FN and register-staged kernels: tile maximum > m + 8):
+      kind "max11" (bf16 LDS-DMA kernel: some x = score - m above 11):
+          the tile's maximum is above M(t) + 11.01;
+      kind "max" (E4M3FN kernels: a lane's sum of P' = 2^(x + c), c <= log2(1.75),
+          above 448; register-staged kernel: tile maximum > m + 8):
           the tile's maximum is above M(t) + 8.01.
     Tile 0 only sets m.  Returns the sorted tile indices t >= 1 at which some row
     forces a rescale; the events hold for any cut of the key range into
     segments, except at a segment's first tile.
     """
+    thr = {"max11": 11.01, "max": 8.01}[kind]
     q = np.asarray(q_vals, np.float64)
     k = np.asarray(k_vals, np.float64)
     d = q.shape[1]
@@ -135,13 +137,7 @@ def rescale_events(q_vals, k_vals, kb, ke, kind, scale=None):
     for t in range(nt):
         cols = np.nonzero(tile == t)[0]
         st = s[:, cols]
-        full = len(cols) == 64
-        if t > 0:
-            if kind == "sum":
-                hit = full and bool(np.any(st.min(axis=1) > run_max + 6.5))
-            else:
-                hit = bool(np.any(st.max(axis=1) > run_max + 8.01))
-            if hit:
-                events.append(t)
+        if t > 0 and bool(np.any(st.max(axis=1) > run_max + thr)):
+            events.append(t)
         run_max = np.maximum(run_max, st.max(axis=1))
     return events

@@ -55,8 +55,8 @@ KE = [6395, 6400, 6340]  # every chunk spans 100 key tiles; chunks 0 and 2 end i
 STEP_KEYS = 256
 
 SPEC = {
-    "pp_tile": dict(dtype="bf16", P=256, ws=False, kernel="dma_bf16", sched="per_tile", kind="sum"),
-    "pp_split": dict(dtype="bf16", P=256, ws=True, kernel="dma_bf16", sched="split", kind="sum"),
+    "pp_tile": dict(dtype="bf16", P=256, ws=False, kernel="dma_bf16", sched="per_tile", kind="max11"),
+    "pp_split": dict(dtype="bf16", P=256, ws=True, kernel="dma_bf16", sched="split", kind="max11"),
     "fp8_tile": dict(dtype="fp8", P=256, ws=False, kernel="dma_fp8", sched="per_tile", kind="max"),
     "fp8_split": dict(dtype="fp8", P=256, ws=True, kernel="dma_fp8", sched="split", kind="max"),
     "staged_bf16": dict(dtype="bf16", P=40, ws=False, kernel="staged_bf16", sched="per_tile", kind="max"),
@@ -341,7 +341,7 @@ def test_peaked_full_window_round_shape(variant):
     qv = values_of(q, "bf16")
     if variant == "staircase":
         K, _ = pair.ref.gather(kb, ke, heads=[0])
-        ev = rescale_events(qv[rows, 0], K[:, 0], kb, ke, "sum")
+        ev = rescale_events(qv[rows, 0], K[:, 0], kb, ke, "max11")
         say("%d tiles force a rescale" % len(ev))
         assert len(ev) >= 20
     o, lse = pair.attend(dev(q, "bf16"), [0, L], [kb], [ke], workspace=ws)

@@ -29,12 +29,12 @@ def test_staircase_rises_by_the_stated_log2_units():
 def test_rescale_event_detector():
     q = synth.normal_f32((64, 1, 128), 0.5, 98, 1)
     k = synth.normal_f32((2048, 1, 128), 0.5, 98, 2)
-    # flat scores: no tile can exceed the running maximum by 6.5 or 8 log2 units
-    assert rescale_events(q[:, 0], k[:, 0], 0, 2048, "sum") == []
+    # flat scores: no tile can exceed the running maximum by 8 or 11 log2 units
+    assert rescale_events(q[:, 0], k[:, 0], 0, 2048, "max11") == []
     assert rescale_events(q[:, 0], k[:, 0], 0, 2048, "max") == []
     qs, ks = synth.staircase(q, k, np.arange(2048), 0, 256, 16.0, seed_words=(98, 3))
-    ev = rescale_events(qs[:, 0], ks[:, 0], 0, 2048, "sum")
+    ev = rescale_events(qs[:, 0], ks[:, 0], 0, 2048, "max11")
     assert ev == [4, 8, 12, 16, 20, 24, 28]          # every step tile of the steepest rows
     assert rescale_events(qs[:, 0], ks[:, 0], 0, 2048, "max") == ev
     # a window starting at 5 keeps the tile grid (base 0); a window ending mid-tile drops no step
-    assert rescale_events(qs[:, 0, :], ks[5:2000, 0], 5, 2000, "sum") == ev
+    assert rescale_events(qs[:, 0, :], ks[5:2000, 0], 5, 2000, "max11") == ev
