@@ -448,7 +448,9 @@ __device__ __forceinline__ void v_phase(f32x16 (&s)[2], i32x8& p8, f32x16 (&o)[D
       g[q] = ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));
 #pragma unroll
       for (int w = 0; w < 2; ++w) {
-        uint32_t v = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(pe[4 * w], pe[4 * w + 1], 0, false);
+        // Both halves of the dword are written; the old value only fills the
+        // half each conversion keeps (the register's own, so no zeroing move).
+        uint32_t v = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(pe[4 * w], pe[4 * w + 1], p8[2 * q + w], false);
         v = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(pe[4 * w + 2], pe[4 * w + 3], (int)v, true);
         p8[2 * q + w] = (int)v;
       }
