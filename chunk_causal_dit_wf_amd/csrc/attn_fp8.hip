@@ -32,12 +32,14 @@
 // tile (phase M), the other runs the softmax of its next tile on the vector
 // unit (phase V).  Every phase ends with a workgroup barrier.
 //   M(t): S(t+1) = K(t+1) Q^T (hi and lo terms, 4 KS MFMAs) and
-//         O^T += V(t)^T P(t) (D / 32 MFMAs).
-//   V(t): the wave's share of the tile loads, then P'(t+1) from S(t+1): the
-//         reference point m of the online softmax moves only when a lane's
-//         sum of P' exceeds 448 (then every P' could still saturate), to the
-//         exact row maximum, with O and l rescaled; the common path takes no
-//         row maximum.
+//         O^T += V(t)^T P(t) (D / 32 MFMAs).  On steady tiles the first step
+//         of the softmax, x = S f + c - m, runs between the P V products:
+//         vector work moved out of phase V, the longer one.
+//   V(t): the wave's share of the tile loads, then P'(t+1) = exp2(x) (e4m3
+//         packing, group sums): the reference point m of the online softmax
+//         moves only when a lane's sum of P' exceeds 448 (then every P' could
+//         still saturate), to the exact row maximum, with O and l rescaled;
+//         the common path takes no row maximum.
 // Tiles stream through a ring of three LDS stages (stage t in slot
 // (t + 1) % 3 holds K(t+1) and V(t)^T), filled by buffer LDS-DMA: group 1
 // loads K tiles four tiles ahead, group 0 V^T tiles two tiles ahead.  K rows

@@ -469,10 +469,12 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(const AttnParams p
 //
 // Per 64-key tile t and wave:
 //   M(t): S(t+1) = K(t+1) Q^T (two 32-key halves, 16 MFMAs) and
-//         O^T += V(t)^T P(t) (16 MFMAs); fragment reads run ahead in LDS.
-//   V(t): issue this wave's share of the tile loads, then row maxima of
-//         S(t+1), the lazy exact rescale, P(t+1) = exp2(S - m) in bf16 and
-//         row sums.
+//         O^T += V(t)^T P(t) (16 MFMAs), plus the row sums of P(t) on the
+//         matrix unit (4 16x16x32 selector products); fragment reads run
+//         ahead in LDS.
+//   V(t): issue this wave's share of the tile loads, then x = S(t+1) sl2 - m,
+//         the guard (largest x), P(t+1) = exp2(x) in bf16, and -- only when
+//         some x exceeds 11 -- the exact rescale.
 //
 // LDS layout.  Rows are padded by 16 bytes (K: 2D+16 bytes, V^T: 144 bytes)
 // so that the lanes one LDS cycle serves hit distinct banks and every
