@@ -89,9 +89,35 @@ def kernel_of(dtype):
     return "attn_fwd_pp_kernel<128>" if dtype == "bf16" else "attn_fwd_fp8_kernel<128>"
 
 
+def code_text(src):
+    """C/C++ source with its comments removed and runs of white space folded to one space, so
+    that an edit of comments or layout alone leaves the hash unchanged."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return re.sub(r"\s+", " ", "".join(out)).strip()
+
+
 def source_sha(name):
-    """sha256 over a kernel source and the local headers it includes (recursively), in include
-    order: a change to any of them invalidates counters taken before it."""
+    """sha256 over the code of a kernel source and of the local headers it includes
+    (recursively), in include order, comments and layout left out: a change to the code of any
+    of them invalidates counters taken before it."""
     csrc = os.path.join(ROOT, "chunk_causal_dit_wf_amd", "csrc")
     seen, order = set(), []
 
@@ -107,8 +133,9 @@ def source_sha(name):
     visit(os.path.join(csrc, name))
     h = hashlib.sha256()
     for path in order:
-        with open(path, "rb") as f:
-            h.update(f.read())
+        with open(path, encoding="utf-8") as f:
+            h.update(code_text(f.read()).encode())
+        h.update(b"\0")
     return h.hexdigest()
 
 

@@ -250,3 +250,19 @@ def test_host_logic_under_address_and_undefined_behavior_sanitizers(tmp_path):
                HIP_VISIBLE_DEVICES="")
     r = subprocess.run([str(tmp_path / "ex")], capture_output=True, text=True, env=env, timeout=300)
     assert r.returncode == 0 and r.stdout.strip().endswith("OK"), (r.stdout[-3000:], r.stderr[-3000:])
+
+
+def test_bench_source_hash_ignores_comments_and_layout_only():
+    """bench.py keeps a committed HBM-traffic figure only while the kernel code it was measured
+    on is unchanged: comments and white space do not count, any code token does."""
+    import bench
+    base = 'int f(int a) {\n  // note\n  return a + 1; /* x */\n}\nconst char* s = "//not a comment";\n'
+    same = 'int f(int a) { return a + 1;\n}   // other note\n/* block */ const char* s = "//not a comment";'
+    diff = 'int f(int a) {\n  return a + 2;\n}\nconst char* s = "//not a comment";\n'
+    lit = 'int f(int a) {\n  return a + 1;\n}\nconst char* s = "//not a Comment";\n'
+    t = bench.code_text(base)
+    assert t == bench.code_text(same)
+    assert t != bench.code_text(diff) and t != bench.code_text(lit)
+    assert "note" not in t and '"//not a comment"' in t
+    for src in ("attn_fwd.hip", "attn_fp8.hip", "kv_cache.hip"):
+        assert re.fullmatch(r"[0-9a-f]{64}", bench.source_sha(src))
