@@ -459,7 +459,8 @@ def extras(args):
                          (PEAK_Q0, PEAK_RISE_LOG2, PEAK_STEP), steps=5)
     r = run_round(sub_args(steps=3, warmup=1), WORKLOADS["fp8round"])
     out["fp8round"] = dict(summary(r, FP8_PEAK_TFLOPS), workload=WORKLOADS["fp8round"]["name"], steps=3,
-                           append_bytes_per_launch=r["append_bytes"])
+                           append_bytes_per_launch=r["append_bytes"], attn_kernel=kernel_of("fp8"),
+                           attn_hbm_traffic=hbm_traffic("attn_fwd_fp8_kernel", "fp8round", "attn_fp8.hip"))
     r = run_round(sub_args(steps=3, warmup=1, quantize_append=True), WORKLOADS["fp8round"])
     out["quantize_append"] = dict(
         kv_append_GBps=round(r["append_gbps"], 1), append_kernel_ms=round(r["append_kernel_ms"], 5),
