@@ -74,8 +74,9 @@ def say(*a):
 class Case:
     """A cache holding N_KEYS keys for one path, the query codes, and the launch arguments."""
 
-    def __init__(self, path, seed, peaked=True, q_mult=1.0, v_ones=False, table=None, fill=True):
+    def __init__(self, path, seed, peaked=True, q_mult=1.0, v_ones=False, table=None, fill=True, d=D):
         sp = SPEC[path]
+        self.D = d
         self.path, self.sp = path, sp
         self.dtype = sp["dtype"]
         P = sp["P"]
@@ -85,15 +86,15 @@ class Case:
         if table is None:
             table = rng.permutation(num_pages)[:T]
         std = 0.5 if self.dtype == "bf16" else 1.0
-        q = synth.normal_f32((Q_OFF[-1], H, D), std, 77, seed, 0)
-        k = synth.normal_f32((N_KEYS, H, D), std, 77, seed, 1)
-        v = synth.normal_f32((N_KEYS, H, D), std, 77, seed, 2)
+        q = synth.normal_f32((Q_OFF[-1], H, d), std, 77, seed, 0)
+        k = synth.normal_f32((N_KEYS, H, d), std, 77, seed, 1)
+        v = synth.normal_f32((N_KEYS, H, d), std, 77, seed, 2)
         if peaked:
             q, k = synth.staircase(q, k, np.arange(N_KEYS), 0, STEP_KEYS, 16.0, seed_words=(77, seed, 3))
         q[:, :, (1 if peaked else 0):] *= np.float32(q_mult)
         if v_ones:
             v[:] = 1.0
-        self.pair = Pair(num_pages, P, H, D, self.dtype, table, fill_seed=seed + 1 if fill else None)
+        self.pair = Pair(num_pages, P, H, d, self.dtype, table, fill_seed=seed + 1 if fill else None)
         if self.dtype == "fp8":
             kc, ks = synth.quantize_e4m3_pages(k, P)
             vc, vs = synth.quantize_e4m3_pages(v, P)
@@ -198,6 +199,21 @@ def test_sharp_queries_every_path(path):
     say("%s: score std %.2f nats, median largest softmax weight %.3f" % (path, s.std(), np.median(top)))
     assert np.median(top) > 0.2
     check_case(case, o, lse, what="sharp Q x%g" % mult)
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_head_dim_64_every_path(path):
+    """head_dim 64 (the kernels' other instantiation) on every path: the peaked staircase against
+    the oracle, and two runs bitwise equal."""
+    say("case: D = 64, peaked staircase, path", path)
+    case = Case(path, seed=46, d=64)
+    case.check_plan()
+    assert len(case.events()) >= 12
+    o, lse = case.attend()
+    check_case(case, o, lse, what="D64 staircase")
+    o2, l2 = case.attend()
+    assert np.array_equal(host_codes(o), host_codes(o2))
+    assert np.array_equal(lse.cpu().numpy(), l2.cpu().numpy())
 
 
 # ----------------------------------------------------------------------------- invariants on every path
