@@ -662,7 +662,9 @@ __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F
 // Zero the keys of V^T tile t (in LDS) that lie outside [lo, hi) (all threads).
 template <int D>
 __device__ __forceinline__ void zero_v_outside(char* vt, int t, int lo, int hi) {
-  for (int idx = threadIdx.x; idx < D * 8; idx += NTD) {
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));  // keep the per-lane keys below out of the tile loop's registers
+  for (int idx = tid; idx < D * 8; idx += NTD) {
     const int d = idx >> 3, c = idx & 7;
     const int rel = t * BN + 8 * c;
     if (rel >= lo && rel + 8 <= hi) continue;
@@ -768,12 +770,19 @@ __device__ __forceinline__ void v_phase(f32x16 (&s)[2], bf16x8 (&pf)[4], f32x16 
                                         f32x4& lacc, float sl2, int kb, int lo, int hi, int hf) {
   typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
   if constexpr (MASK) {
+    // Element e of half h holds key kb + HK h + 16 hf + e.  The lane's part
+    // 16 hf is made opaque here so that the compiler keeps the 32 per-element
+    // keys inside this (rare) block instead of hoisting them out of the tile
+    // loop into registers it would then spill.
+    int lane_key = 16 * hf;
+    asm volatile("" : "+v"(lane_key));
+    const int lo_r = lo - kb, hi_r = hi - kb;
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int key = kb + HK * h + 16 * hf + e;  // key of S^T element e
-        s[h][e] = (key >= lo && key < hi) ? s[h][e] : -INFINITY;
+        const int key = lane_key + (HK * h + e);
+        s[h][e] = (key >= lo_r && key < hi_r) ? s[h][e] : -INFINITY;
       }
   }
   auto row_max = [&]() {
