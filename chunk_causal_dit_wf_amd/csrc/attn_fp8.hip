@@ -197,12 +197,19 @@ __device__ __forceinline__ void zero_v_outside(char* vt, int t, int lo, int hi) 
     const int d = idx >> 2, c = idx & 3;
     const int rel = t * TK + 16 * c;
     if (rel >= lo && rel + 16 <= hi) continue;
+    // Keys rel + e with e in [ka, kb) stay; their bytes are kept by a mask
+    // built from the bit range (no per-key compares: sixteen per-lane key
+    // constants would be hoisted out of the tile loop and spilled).
+    const int ka = min(max(lo - rel, 0), 16), kb = min(max(hi - rel, 0), 16);
+    const uint32_t keep = kb > ka ? (((1u << kb) - 1u) & ~((1u << ka) - 1u)) : 0u;
     uint4* a = (uint4*)(vt + d * Geo<D>::VROW + 16 * c);
     const uint4 v = *a;
     uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-    for (int e = 0; e < 16; ++e)
-      if (!(rel + e >= lo && rel + e < hi)) w[e >> 2] &= ~(0xFFu << (8 * (e & 3)));
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t n = (keep >> (4 * q)) & 0xFu;        // bit j: byte j of word q stays
+      w[q] &= ((n * 0x00204081u) & 0x01010101u) * 0xFFu;  // bit j -> byte j
+    }
     *a = make_uint4(w[0], w[1], w[2], w[3]);
   }
 }
