@@ -320,26 +320,29 @@ __device__ __forceinline__ void m_phase(f32x16 (&s)[2], f32x16 (&o)[D / 32], con
   static_assert(DB == 2 * KS, "two PV products per k-block");
   static_assert(!XPRE || (QK && PV), "XPRE needs both products");
   if constexpr (XPRE) {
-    i32x8 fa = k_frag<D>(kt, kx, 0, 0), fb = k_frag<D>(kt, kx, 1, 0);
-    static_for<KS>([&](auto KB) {
-      constexpr int kb = decltype(KB)::value;
-      if constexpr (kb == 0) {
-        s[0] = mfma8z(fa, qh[0]);
-        s[1] = mfma8z(fb, qh[0]);
-      } else {
-        s[0] = mfma8(fa, qh[kb], s[0]);
-        s[1] = mfma8(fb, qh[kb], s[1]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      s[0] = mfma8(fa, ql[kb], s[0]);
-      if constexpr (kb + 1 < KS) fa = k_frag<D>(kt, kx, 0, kb + 1);
-      s[1] = mfma8(fb, ql[kb], s[1]);
-      if constexpr (kb + 1 < KS) fb = k_frag<D>(kt, kx, 1, kb + 1);
-      __builtin_amdgcn_sched_barrier(0);
-    });
+    // Products in issue order: Q K^T (half h, k-block kb, term) as
+    // [hi h0, hi h1, lo h0, lo h1] per kb, then the DB P V products.  Every
+    // fragment read is issued PF products before the product that first uses it.
+    constexpr int NQ = 4 * KS;
+    constexpr int NL = 2 * KS + DB;  // fragment reads: K (h, kb) in kb-major order, then V (db)
+    constexpr int PF = 3;
+    i32x8 kf[2][KS];
+    i32x8 vf[DB];
+    auto first_use = [](int j) { return j < 2 * KS ? 4 * (j / 2) + j % 2 : NQ + (j - 2 * KS); };
+    auto issue_for = [&](auto I) {  // the reads due before product I
+      constexpr int i = decltype(I)::value;
+      static_for<NL>([&](auto J) {
+        constexpr int j = decltype(J)::value;
+        constexpr int due = first_use(j) - PF;
+        if constexpr ((i == 0 && due <= 0) || (i > 0 && due == i)) {
+          if constexpr (j < 2 * KS)
+            kf[j % 2][j / 2] = k_frag<D>(kt, kx, j % 2, j / 2);
+          else
+            vf[j - 2 * KS] = v_frag<D>(vt, vx, j - 2 * KS);
+        }
+      });
+    };
     float cm[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) cm[q] = F->c[q] - m;
     // With four P V products the first three are each followed by the x of
     // PER elements of S (the last product then runs while the phase ends);
     // with two, each by 16.  Either way no x reads s[h] sooner than two
@@ -347,19 +350,32 @@ __device__ __forceinline__ void m_phase(f32x16 (&s)[2], f32x16 (&o)[D / 32], con
     // such a product has returned its old value on this hardware, although
     // the compiler's wait states allow it.
     constexpr int PER = DB > 2 ? (32 + DB - 2) / (DB - 1) : 32 / DB;
-    i32x8 fv = v_frag<D>(vt, vx, 0);
-    static_for<DB>([&](auto DBI) {
-      constexpr int db = decltype(DBI)::value;
-      const i32x8 f = fv;
-      if constexpr (db + 1 < DB) fv = v_frag<D>(vt, vx, db + 1);
-      o[db] = mfma8(f, p8, o[db]);
-      static_for<PER>([&](auto I) {
-        constexpr int i = PER * db + decltype(I)::value;
-        if constexpr (i < 32) {
-          constexpr int h = i / 16, e = i % 16;
-          s[h][e] = __builtin_fmaf(s[h][e], F->f[2 * h + e / 8], cm[2 * h + e / 8]);
+    static_for<NQ + DB>([&](auto I) {
+      constexpr int i = decltype(I)::value;
+      issue_for(I);
+      if constexpr (i < NQ) {
+        constexpr int kb = i / 4, h = i % 2;
+        if constexpr ((i % 4) >= 2)
+          s[h] = mfma8(kf[h][kb], ql[kb], s[h]);
+        else if constexpr (kb == 0)
+          s[h] = mfma8z(kf[h][kb], qh[0]);
+        else
+          s[h] = mfma8(kf[h][kb], qh[kb], s[h]);
+        if constexpr (i == NQ - 1) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) cm[q] = F->c[q] - m;
         }
-      });
+      } else {
+        constexpr int db = i - NQ;
+        o[db] = mfma8(vf[db], p8, o[db]);
+        static_for<PER>([&](auto E) {
+          constexpr int k = PER * db + decltype(E)::value;
+          if constexpr (k < 32) {
+            constexpr int h = k / 16, e = k % 16;
+            s[h][e] = __builtin_fmaf(s[h][e], F->f[2 * h + e / 8], cm[2 * h + e / 8]);
+          }
+        });
+      }
       __builtin_amdgcn_sched_barrier(0);
     });
   } else if constexpr (QK) {
