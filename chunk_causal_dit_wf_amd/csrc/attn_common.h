@@ -30,14 +30,10 @@ __device__ __forceinline__ float half_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Work item -> (chunk, query tile, head).  The dispatcher deals workgroups
-// round-robin over the 8 XCDs (workgroup g to XCD g % 8), and each XCD has its
-// own L2.  All query tiles of one (chunk, head) read the same keys, so inside
-// a chunk (N = tiles x H items, local index L) the items are dealt so that XCD
-// x = L % 8 takes a contiguous run of the head-major order (head, tile): runs
-// of Q + 1 items for x < R and Q for the rest (N = 8 Q + R); the k-th
-// workgroup of XCD x (k = L / 8) takes position start(x) + k.  Workgroups that
-// run together on one XCD then share one or two heads' keys in its L2.
+// Work item -> (chunk, query tile, head).  All query tiles of one (chunk,
+// head) read the same keys, and each of the 8 XCDs has its own L2, so inside
+// a chunk the items are dealt (deal_position) so that the workgroups that run
+// together on one XCD share as few heads' keys as possible.
 struct Item {
   int c, qt, head;
 };
@@ -50,11 +46,7 @@ __device__ __forceinline__ Item decode_item(const AttnParams& p, int item) {
   Item it;
   it.c = chunk_of_item(p, item);
   const int T = p.chunk[it.c].ntiles;
-  const int N = T * p.H;
-  const int L = item - p.chunk[it.c].item0;
-  const int Q = N >> 3, R = N & 7;
-  const int x = L & 7, k = L >> 3;
-  const int pos = x * Q + min(x, R) + k;
+  const int pos = deal_position(T * p.H, item - p.chunk[it.c].item0);
   it.head = pos / T;
   it.qt = pos - it.head * T;
   return it;
@@ -62,18 +54,7 @@ __device__ __forceinline__ Item decode_item(const AttnParams& p, int item) {
 // Inverse of decode_item inside chunk c: (query tile, head) -> item.
 __device__ __forceinline__ int encode_item(const AttnParams& p, int c, int qt, int head) {
   const int T = p.chunk[c].ntiles;
-  const int N = T * p.H;
-  const int Q = N >> 3, R = N & 7;
-  const int pos = head * T + qt;
-  int x, k;
-  if (pos < R * (Q + 1)) {
-    x = pos / (Q + 1);
-    k = pos - x * (Q + 1);
-  } else {
-    x = R + (pos - R * (Q + 1)) / Q;
-    k = pos - R * (Q + 1) - (x - R) * Q;
-  }
-  return p.chunk[c].item0 + 8 * k + x;
+  return p.chunk[c].item0 + deal_index(T * p.H, head * T + qt);
 }
 
 constexpr float kRescaleThreshold = 8.0f;  // log2 units: p <= 2^8 between rescales

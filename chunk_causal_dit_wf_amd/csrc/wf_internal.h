@@ -37,6 +37,39 @@ __host__ __device__ inline uint32_t fastdiv(uint32_t n, const FastDiv& f) {
   return (t + ((n - t) >> 1)) >> (f.shift - 1);
 }
 
+// XCD deal of a chunk's N work items (head-major positions 0 .. N-1).  The
+// dispatcher sends workgroup L to XCD L % 8, so XCD x runs Q + 1 workgroups
+// for x < R and Q for the rest (N = 8 Q + R).  The head-major order is cut
+// into 8 runs with evenly spread ends, run r = [start(r), start(r + 1)),
+// start(r) = floor((N r + 4) / 8), so that run ends fall on head ends where
+// they can (each head's keys then sit in as few L2s as possible); run r is
+// long (Q + 1 items) iff (R r + 4) mod 8 >= 8 - R.  XCD x < R takes the x-th
+// long run, XCD x >= R the (x - R)-th short one, and its k-th workgroup
+// (k = L / 8) the k-th position of that run.
+__host__ __device__ inline int deal_run_start(int N, int r) { return (int)(((int64_t)N * r + 4) >> 3); }
+__host__ __device__ inline bool deal_run_long(int R, int r) { return ((R * r + 4) & 7) >= 8 - R; }
+
+// Workgroup index L (0 <= L < N) -> head-major position.
+__host__ __device__ inline int deal_position(int N, int L) {
+  const int R = N & 7, x = L & 7, k = L >> 3;
+  const bool lng = x < R;
+  int idx = lng ? x : x - R, r = 0;
+  for (; r < 8; ++r)
+    if (deal_run_long(R, r) == lng && idx-- == 0) break;
+  return deal_run_start(N, r) + k;
+}
+
+// Inverse: head-major position (0 <= pos < N) -> workgroup index L.
+__host__ __device__ inline int deal_index(int N, int pos) {
+  const int R = N & 7;
+  int r = 0;
+  while (r < 7 && deal_run_start(N, r + 1) <= pos) ++r;
+  const bool lng = deal_run_long(R, r);
+  int rank = 0;
+  for (int q = 0; q < r; ++q) rank += deal_run_long(R, q) == lng;
+  return 8 * (pos - deal_run_start(N, r)) + (lng ? rank : R + rank);
+}
+
 // Page addressing of a window that starts at a known logical position.  For a
 // logical token t >= base, with rel = t - base (32-bit):
 //   slot   = (base_slot + (base_off + rel) / P) mod T

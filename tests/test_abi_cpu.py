@@ -208,6 +208,48 @@ int main() {
     assert out.returncode == 0 and out.stdout.strip() == "0"
 
 
+def test_xcd_deal_is_a_bijection_on_host(tmp_path):
+    """The attention kernels' item deal (wf_internal.h): for every chunk size N up to 5000 it is
+    a bijection of [0, N) whose inverse is deal_index, XCD x = L % 8 runs one contiguous run of
+    the head-major order, and for the Wan round (19 query tiles x 12 heads) the 8 XCDs hold 16
+    (XCD, head) pairs, the fewest possible (at most 32 items fit one XCD, so 4 heads must split)."""
+    src = r"""
+#include <cstdio>
+#include <vector>
+#include <set>
+#include "wf_internal.h"
+int main() {
+  long bad = 0;
+  for (int N = 1; N <= 5000; ++N) {
+    std::vector<int> seen(N, 0), lo(8, N), hi(8, -1), cnt(8, 0);
+    for (int L = 0; L < N; ++L) {
+      const int pos = wf::deal_position(N, L);
+      if (pos < 0 || pos >= N) { ++bad; continue; }
+      seen[pos]++;
+      bad += wf::deal_index(N, pos) != L;
+      const int x = L & 7;
+      lo[x] = pos < lo[x] ? pos : lo[x]; hi[x] = pos > hi[x] ? pos : hi[x]; cnt[x]++;
+    }
+    for (int i = 0; i < N; ++i) bad += seen[i] != 1;
+    for (int x = 0; x < 8; ++x) if (cnt[x]) bad += hi[x] - lo[x] + 1 != cnt[x];  // contiguous run
+  }
+  std::set<std::pair<int, int>> pairs;
+  for (int L = 0; L < 228; ++L) pairs.insert({L & 7, wf::deal_position(228, L) / 19});
+  printf("%ld %zu\n", bad, pairs.size());
+  return bad != 0;
+}
+"""
+    c = tmp_path / "t.hip"
+    c.write_text(src)
+    exe = tmp_path / "t"
+    r = subprocess.run(["/opt/rocm/bin/hipcc", "-O2", "-I", os.path.join(ROOT, "chunk_causal_dit_wf_amd", "csrc"),
+                        "--offload-arch=gfx950", "-x", "hip", str(c), "-o", str(exe)],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    out = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert out.returncode == 0 and out.stdout.split() == ["0", "16"], out.stdout
+
+
 def test_quantizing_append_validation():
     k = torch.zeros(64, 2, 64, dtype=torch.bfloat16)
     b = _cache("bf16")
