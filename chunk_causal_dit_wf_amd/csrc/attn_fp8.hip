@@ -30,7 +30,9 @@
 // chunk; waves 0-3 (group 0) and 4-7 (group 1) run the same program one phase
 // apart, so while one wave of a SIMD issues the matrix products of a 64-key
 // tile (phase M), the other runs the softmax of its next tile on the vector
-// unit (phase V).  Every phase ends with a workgroup barrier.
+// unit (phase V).  Every phase ends with a workgroup barrier; the wave in
+// phase V runs at the higher wave priority (prio).  Fragment reads of a steady
+// phase M run three products ahead of their use.
 //   M(t): S(t+1) = K(t+1) Q^T (hi and lo terms, 4 KS MFMAs) and
 //         O^T += V(t)^T P(t) (D / 32 MFMAs).  On steady tiles the first step
 //         of the softmax, x = S f + c - m, runs between the P V products:

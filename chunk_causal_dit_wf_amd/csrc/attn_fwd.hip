@@ -465,7 +465,8 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(const AttnParams p
 // one wave of a SIMD issues the matrix products of a 64-key tile (phase M),
 // the other computes the softmax of its next tile on the vector unit (phase
 // V).  Every phase ends with a workgroup barrier, so the offset never drifts
-// and the matrix unit of each SIMD always has one wave feeding it.
+// and the matrix unit of each SIMD always has one wave feeding it; the wave
+// in phase V runs at the higher wave priority (prio).
 //
 // Per 64-key tile t and wave:
 //   M(t): S(t+1) = K(t+1) Q^T (two 32-key halves, 16 MFMAs) and
