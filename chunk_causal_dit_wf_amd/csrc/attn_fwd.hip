@@ -470,12 +470,12 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(const AttnParams p
 //
 // Per 64-key tile t and wave:
 //   M(t): S(t+1) = K(t+1) Q^T (two 32-key halves, 16 MFMAs) and
-//         O^T += V(t)^T P(t) (16 MFMAs), plus the row sums of P(t) on the
-//         matrix unit (4 16x16x32 selector products); fragment reads run
-//         ahead in LDS.
+//         O^T += V(t)^T P(t) (16 MFMAs); fragment reads run ahead in LDS.
 //   V(t): issue this wave's share of the tile loads, then x = S(t+1) sl2 - m,
 //         the guard (largest x), P(t+1) = exp2(x) in bf16, and -- only when
-//         some x exceeds 11 -- the exact rescale.
+//         some x exceeds 11 -- the exact rescale; then the row sums of
+//         P(t+1) on the matrix unit (4 16x16x32 selector products, which the
+//         SIMD's matrix pipe runs between the other wave's products).
 //
 // LDS layout.  Rows are padded by 16 bytes (K: 2D+16 bytes, V^T: 144 bytes)
 // so that the lanes one LDS cycle serves hit distinct banks and every
@@ -707,14 +707,13 @@ __device__ __forceinline__ bf16x8 row_sum_selector(int lane) {
 }
 
 // Phase M of one 64-key tile.  QK: S(t+1) = K(t+1) Q^T from the K tile at kt
-// (two halves into s[0], s[1]).  PV: O^T += V(t)^T P(t) from the V tile at vt,
-// and lacc += the row sums of P(t) (one 16x16x32 product per P fragment).
+// (two halves into s[0], s[1]).  PV: O^T += V(t)^T P(t) from the V tile at vt.
 // kx / vx: this lane's LDS byte offsets of its K row chunk and of its V^T row
 // chunk.  Fragment reads run DIST products ahead of their use.
 template <int D, bool QK, bool PV>
 __device__ __forceinline__ void m_phase(f32x16 (&s)[2], f32x16 (&o)[D / 32], const bf16x8 (&qf)[D / 16],
                                         const bf16x8 (&pf)[4], const char* kt, const char* vt, int kx, int vx,
-                                        const bf16x8& sel, f32x4& lacc) {
+                                        f32x4& lacc) {
   using G = Geo<D>;
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
@@ -752,7 +751,6 @@ __device__ __forceinline__ void m_phase(f32x16 (&s)[2], f32x16 (&o)[D / 32], con
     } else {
       const int j = 2 * ks + (r - (QK ? 2 : 0));
       o[j % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, pf[j / DB], o[j % DB], 0, 0, 0);
-      if (j % DB == DB - 1) lacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, pf[j / DB], lacc, 0, 0, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -762,6 +760,8 @@ __device__ __forceinline__ void m_phase(f32x16 (&s)[2], f32x16 (&o)[D / 32], con
   if constexpr (PV) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) asm volatile("" : "+v"(o[db]));
+    // The row sums are taken in phase V, but pinning them here as well
+    // measured 1-2 % faster than leaving them free.
     asm volatile("" : "+v"(lacc));
   }
 }
@@ -774,14 +774,15 @@ __device__ __forceinline__ void m_phase(f32x16 (&s)[2], f32x16 (&o)[D / 32], con
 // exactly before P is formed again.  Every p stays at most 2^11 (no overflow;
 // bf16 keeps its relative precision), and the common path needs no exact
 // maximum: the guard is a max3 tree over x, which does not wait for the
-// exponentials.  The row sums themselves are taken on the matrix unit in phase
-// M (row_sum_selector).  FIRST: the first tile of a segment sets m from its own
+// exponentials.  The row sums of the new P are taken on the matrix unit at
+// the end of the phase (row_sum_selector).  FIRST: the first tile of a segment sets m from its own
 // row maxima.  MASK: keys outside [lo, hi) (tile-relative key kb + ...) are
 // set to -inf first.  Each step is applied to all 32 elements before the next:
 // independent instructions cover each other's latency.
 template <int D, bool MASK, bool FIRST>
 __device__ __forceinline__ void v_phase(f32x16 (&s)[2], bf16x8 (&pf)[4], f32x16 (&o)[D / 32], float& m,
-                                        f32x4& lacc, float sl2, int kb, int lo, int hi, int hf) {
+                                        f32x4& lacc, const bf16x8& sel, float sl2, int kb, int lo, int hi,
+                                        int hf) {
   typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
   if constexpr (MASK) {
     // Element e of half h holds key kb + HK h + 16 hf + e.  The lane's part
@@ -855,6 +856,9 @@ __device__ __forceinline__ void v_phase(f32x16 (&s)[2], bf16x8 (&pf)[4], f32x16 
     lacc[1] *= alpha_hi;
     form_p();
   }
+  // Row sums of the new P on the matrix unit (row_sum_selector).
+#pragma unroll
+  for (int q = 0; q < 4; ++q) lacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, pf[q], lacc, 0, 0, 0);
   // Keep the softmax in this phase.
   asm volatile("" : "+v"(pf[0]), "+v"(pf[1]), "+v"(pf[2]), "+v"(pf[3]), "+v"(lacc));
 }
@@ -977,13 +981,13 @@ __device__ __forceinline__ void segment(const AttnParams& p, const ChunkDesc& cd
   barrier();
   if (group == 1) barrier();  // group 1 runs one phase behind
   // M(-1): S(0) from K(0) in slot 0.
-  m_phase<D, true, false>(s, o, qf, pf, rg.k<0>(), rg.v<0>(), kx, vx, sel, lacc);
+  m_phase<D, true, false>(s, o, qf, pf, rg.k<0>(), rg.v<0>(), kx, vx, lacc);
   end_phase();
   if (group == 1 && vedge(0)) zero_v(rg.v<1>(), 0);
   // V(-1)
   prio(1);  // the softmax wave issues first on its SIMD
   loads(-1, rg.v<2>(), rg.k<0>());
-  v_phase<D, true, true>(s, pf, o, m, lacc, sl2, 0, lo, hi, hf);
+  v_phase<D, true, true>(s, pf, o, m, lacc, sel, sl2, 0, lo, hi, hf);
   prio(0);
   end_phase();
   if (group == 0 && vedge(0)) zero_v(rg.v<1>(), 0);
@@ -997,11 +1001,11 @@ __device__ __forceinline__ void segment(const AttnParams& p, const ChunkDesc& cd
   auto steady = [&](auto rho_tag, int t) {
     constexpr int rho = decltype(rho_tag)::value;
     constexpr int sl = (rho + 1) % 3;
-    m_phase<D, true, true>(s, o, qf, pf, rg.k<sl>(), rg.v<sl>(), kx, vx, sel, lacc);
+    m_phase<D, true, true>(s, o, qf, pf, rg.k<sl>(), rg.v<sl>(), kx, vx, lacc);
     end_phase();
     prio(1);  // the softmax wave issues first on its SIMD
     loads(t, rg.v<rho>(), rg.k<sl>());
-    v_phase<D, false, false>(s, pf, o, m, lacc, sl2, 0, lo, hi, hf);
+    v_phase<D, false, false>(s, pf, o, m, lacc, sel, sl2, 0, lo, hi, hf);
     prio(0);
     end_phase();
   };
@@ -1009,13 +1013,13 @@ __device__ __forceinline__ void segment(const AttnParams& p, const ChunkDesc& cd
     constexpr int rho = decltype(rho_tag)::value;
     constexpr int sl = (rho + 1) % 3;
     constexpr int sn = (rho + 2) % 3;  // slot of stage t + 1
-    m_phase<D, true, true>(s, o, qf, pf, rg.k<sl>(), rg.v<sl>(), kx, vx, sel, lacc);
+    m_phase<D, true, true>(s, o, qf, pf, rg.k<sl>(), rg.v<sl>(), kx, vx, lacc);
     end_phase();
     const bool ze = vedge(t + 1);
     if (group == 1 && ze) zero_v(rg.v<sn>(), t + 1);
     prio(1);  // the softmax wave issues first on its SIMD
     loads(t, rg.v<rho>(), rg.k<sl>());
-    v_phase<D, true, false>(s, pf, o, m, lacc, sl2, BN * (t + 1), lo, hi, hf);
+    v_phase<D, true, false>(s, pf, o, m, lacc, sel, sl2, BN * (t + 1), lo, hi, hf);
     prio(0);
     end_phase();
     if (group == 0 && ze) zero_v(rg.v<sn>(), t + 1);
@@ -1049,7 +1053,7 @@ __device__ __forceinline__ void segment(const AttnParams& p, const ChunkDesc& cd
   {
     const int sl = nt % 3;
     const char* vt = sl == 0 ? rg.v0 : sl == 1 ? rg.v1 : rg.v2;
-    m_phase<D, false, true>(s, o, qf, pf, rg.k0, vt, kx, vx, sel, lacc);
+    m_phase<D, false, true>(s, o, qf, pf, rg.k0, vt, kx, vx, lacc);
     __builtin_amdgcn_s_sleep(2);
     end_phase();
   }
