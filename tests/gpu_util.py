@@ -141,3 +141,17 @@ def rescale_events(q_vals, k_vals, kb, ke, kind, scale=None):
             events.append(t)
         run_max = np.maximum(run_max, st.max(axis=1))
     return events
+
+
+def score_error_bounds(q_vals, K, q_off, kb, ke, kb0):
+    """Delta_row per (head, row): 2^-8 * scale * max over the row's visible keys of sum_d |q_d k_jd|."""
+    qa = np.abs(np.asarray(q_vals, np.float64))
+    ka = np.abs(np.asarray(K, np.float64))
+    nq, h, d = qa.shape
+    out = np.zeros((h, nq))
+    for c in range(len(q_off) - 1):
+        a, b = kb[c] - kb0, ke[c] - kb0
+        for hh in range(h):
+            m = qa[q_off[c]:q_off[c + 1], hh] @ ka[a:b, hh].T
+            out[hh, q_off[c]:q_off[c + 1]] = m.max(axis=1) if m.size else 0.0
+    return out * 2.0 ** -8 / np.sqrt(d)

@@ -43,7 +43,7 @@ import torch
 
 import chunk_causal_dit_wf_amd as wf
 import synth
-from gpu_util import Pair, dev, errors, host_codes, host_values, rescale_events, values_of
+from gpu_util import Pair, dev, errors, host_codes, host_values, rescale_events, score_error_bounds, values_of
 
 pytestmark = pytest.mark.gpu
 
@@ -125,20 +125,6 @@ class Case:
                 rows = qv[Q_OFF[c]:Q_OFF[c + 1], h]
                 ev |= set(rescale_events(rows, K[KB[c]:KE[c], h], KB[c], KE[c], self.sp["kind"]))
         return sorted(ev)
-
-
-def score_error_bounds(q_vals, K, q_off, kb, ke, kb0):
-    """Delta_row per (head, row): 2^-8 * scale * max over the row's visible keys of sum_d |q_d k_jd|."""
-    qa = np.abs(np.asarray(q_vals, np.float64))
-    ka = np.abs(np.asarray(K, np.float64))
-    nq, h, d = qa.shape
-    out = np.zeros((h, nq))
-    for c in range(len(q_off) - 1):
-        a, b = kb[c] - kb0, ke[c] - kb0
-        for hh in range(h):
-            m = qa[q_off[c]:q_off[c + 1], hh] @ ka[a:b, hh].T
-            out[hh, q_off[c]:q_off[c + 1]] = m.max(axis=1) if m.size else 0.0
-    return out * 2.0 ** -8 / np.sqrt(d)
 
 
 def check_bars(kernel_dtype, staged, got, ref, lse, rl, what, q_vals=None, K=None, V=None, args=None):
