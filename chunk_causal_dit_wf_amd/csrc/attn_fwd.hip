@@ -997,7 +997,7 @@ __device__ __forceinline__ void segment(const AttnParams& p, const ChunkDesc& cd
   // the LDS-DMA targets from the buffers being read); every call site below
   // has a static ring position.  steady(t) needs t + 2 < nt: S(t+1) needs no
   // mask and V tile t+1 no zeroing.  edge_step(t) is tile nt - 2; tile nt - 1
-  // follows the switch.
+  // follows the steps.
   auto steady = [&](auto rho_tag, int t) {
     constexpr int rho = decltype(rho_tag)::value;
     constexpr int sl = (rho + 1) % 3;
@@ -1024,27 +1024,31 @@ __device__ __forceinline__ void segment(const AttnParams& p, const ChunkDesc& cd
     end_phase();
     if (group == 0 && ze) zero_v(rg.v<sn>(), t + 1);
   };
-  int t = 0;
-  for (; t + 4 < nt; t += 3) {
-    steady(IC<0>{}, t);
-    steady(IC<1>{}, t + 1);
-    steady(IC<2>{}, t + 2);
-  }
-  switch (nt - t) {  // 1 .. 4 tiles left, t % 3 == 0
-    case 1:
-      break;
-    case 2:
-      edge_step(IC<0>{}, t);
-      break;
-    case 3:
-      steady(IC<0>{}, t);
-      edge_step(IC<1>{}, t + 1);
-      break;
-    default:
+  // Steps 0 .. nt - 3 are steady, step nt - 2 the edge step.  Each residue
+  // R = (nt - 2) % 3 runs its own copy of the loop and of the steps after it.
+  // (One loop shared by the four remainders spilled 424 bytes per lane where
+  // the remainders joined, about 60 MB of scratch traffic per Wan-round
+  // launch; with a copy per residue nothing spills.)
+  auto run = [&](auto r_tag) {
+    constexpr int R = decltype(r_tag)::value;
+    int t = 0;
+    for (; t + R + 2 < nt; t += 3) {
       steady(IC<0>{}, t);
       steady(IC<1>{}, t + 1);
-      edge_step(IC<2>{}, t + 2);
-      break;
+      steady(IC<2>{}, t + 2);
+    }
+    if constexpr (R >= 1) steady(IC<0>{}, t);
+    if constexpr (R >= 2) steady(IC<1>{}, t + 1);
+    edge_step(IC<R>{}, t + R);
+  };
+  if (nt >= 2) {
+    const int r = (nt - 2) % 3;
+    if (r == 0)
+      run(IC<0>{});
+    else if (r == 1)
+      run(IC<1>{});
+    else
+      run(IC<2>{});
   }
   // Tile nt - 1: its P V product alone, from slot nt % 3 (one code path for
   // every tile count).  The epilogue reads the accumulators with plain VALU
