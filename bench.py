@@ -383,28 +383,40 @@ def copy_calibration(nbytes, nbuf=30, reps=3):
     """Achievable rate of a plain device copy moving the append's bytes (read nbytes, write nbytes),
     over nbuf distinct source/destination pairs (the rounds' per-layer rotation, so no copy is served
     from the previous one's lines in the 256 MB MALL): the practical HBM ceiling for a single
-    kernel of the append's size, launch and ramp included."""
+    kernel of the append's size, launch and ramp included.  Two copies are timed: torch's copy_ and
+    the library's wf_stream_copy (persistent grid, nontemporal 16-byte loads and stores, the
+    fastest copy shape measured at this size)."""
     import torch
+    import chunk_causal_dit_wf_amd as wf
+    nbytes -= nbytes % 16
     src = [torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(i) for i in range(nbuf)]
     dst = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(nbuf)]
-    for a, b in zip(src, dst):
-        b.copy_(a)
-    torch.cuda.synchronize()
-    ms = []
-    for _ in range(reps):
+
+    def timed(copy):
         for a, b in zip(src, dst):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            b.copy_(a)
-            e1.record()
-            ms.append((e0, e1))
-    torch.cuda.synchronize()
-    t = sorted(a.elapsed_time(b) for a, b in ms)
-    med = t[len(t) // 2]
+            copy(a, b)
+        torch.cuda.synchronize()
+        ms = []
+        for _ in range(reps):
+            for a, b in zip(src, dst):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                copy(a, b)
+                e1.record()
+                ms.append((e0, e1))
+        torch.cuda.synchronize()
+        t = sorted(a.elapsed_time(b) for a, b in ms)
+        med = t[len(t) // 2]
+        return dict(GBps=round(2 * nbytes / (med * 1e-3) / 1e9, 1), ms=round(med, 5), copies=len(t))
+
+    out = timed(lambda a, b: b.copy_(a))
+    out.update(bytes_per_copy=2 * nbytes, kernel="torch copy_ (a plain device copy kernel)")
+    sc = timed(lambda a, b: wf.wf_stream_copy(a, b))
+    sc["kernel"] = "wf_stream_copy (persistent grid, nontemporal 16-byte loads and stores)"
+    out["stream_copy"] = sc
     del src, dst
     torch.cuda.empty_cache()
-    return dict(GBps=round(2 * nbytes / (med * 1e-3) / 1e9, 1), ms=round(med, 5), bytes_per_copy=2 * nbytes,
-                copies=len(t), kernel="torch copy_ (a plain device copy kernel)")
+    return out
 
 
 def cpu_baseline(rows, H, D, keys):
@@ -535,6 +547,7 @@ def main():
         if not args.no_extras:
             cal = copy_calibration(r["append_bytes"] // 2)
             cal["append_frac_of_copy"] = round(r["append_gbps"] / cal["GBps"], 4)
+            cal["append_frac_of_stream_copy"] = round(r["append_gbps"] / cal["stream_copy"]["GBps"], 4)
             out["append_roofline"]["copy_calibration"] = cal
     if r.get("graph"):
         out["graph_replay"] = r["graph"]

@@ -82,8 +82,10 @@ def lib():
                                                 ctypes.POINTER(i64), f32, vp]
         L.wf_chunk_attn_plan.argtypes = [P, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i64), ctypes.POINTER(i64),
                                          ctypes.c_uint64, ctypes.POINTER(wf_attn_plan)]
+        L.wf_stream_copy.argtypes = [vp, vp, ctypes.c_uint64, vp]
         for name in ("wf_kv_cache_check", "wf_kv_cache_bytes", "wf_kv_append", "wf_kv_evict", "wf_chunk_attn_fwd",
-                     "wf_chunk_attn_workspace_bytes", "wf_kv_append_quantize", "wf_chunk_attn_plan", "wf_chunk_attn_fwd_noalloc"):
+                     "wf_chunk_attn_workspace_bytes", "wf_kv_append_quantize", "wf_chunk_attn_plan", "wf_chunk_attn_fwd_noalloc",
+                     "wf_stream_copy"):
             getattr(L, name).restype = ctypes.c_int
         L.wf_last_error.restype = ctypes.c_char_p
         L.wf_last_error.argtypes = []
@@ -178,6 +180,12 @@ def wf_kv_append_quantize(cache, pos, k_new, v_new, stream=None):
 
 def wf_kv_evict(cache, n, poison=False, stream=None):
     _check(lib().wf_kv_evict(ctypes.byref(cache.c), int(n), WF_EVICT_POISON if poison else 0, _stream(stream)))
+
+
+def wf_stream_copy(src, dst, nbytes=None, stream=None):
+    """Measurement aid: copy nbytes (default: all of src) from tensor src to tensor dst."""
+    n = src.numel() * src.element_size() if nbytes is None else int(nbytes)
+    _check(lib().wf_stream_copy(_ptr(src), _ptr(dst), n, _stream(stream)))
 
 
 def wf_chunk_attn_workspace_bytes(cache):

@@ -11,6 +11,7 @@
 #include <string>
 #include <vector>
 
+#include "copy_ref.h"
 #include "wf_internal.h"
 
 namespace {
@@ -260,6 +261,18 @@ wf_status wf_kv_append_quantize(wf_kv_cache* c, int64_t pos, int32_t n, const vo
   hipError_t e = wf::launch_quant_append(p, (hipStream_t)stream);
   if (e != hipSuccess) return fail(WF_ERR_HIP, "quantising append launch failed: %s", hipGetErrorString(e));
   c->end = std::max(c->end, pos + n);
+  return ok();
+}
+
+wf_status wf_stream_copy(const void* src, void* dst, uint64_t bytes, void* stream) {
+  if (bytes == 0) return ok();
+  if (src == nullptr || dst == nullptr) return fail(WF_ERR_INVALID_ARG, "stream copy: null pointer");
+  if (bytes % 16 != 0 || ((uintptr_t)src | (uintptr_t)dst) % 16 != 0)
+    return fail(WF_ERR_INVALID_ARG, "stream copy: size and pointers must be multiples of 16 bytes");
+  const uintptr_t a = (uintptr_t)src, b = (uintptr_t)dst;
+  if (a < b + bytes && b < a + bytes) return fail(WF_ERR_INVALID_ARG, "stream copy: buffers overlap");
+  hipError_t e = wf::launch_stream_copy(src, dst, (int64_t)(bytes / 16), (hipStream_t)stream);
+  if (e != hipSuccess) return fail(WF_ERR_HIP, "stream copy launch failed: %s", hipGetErrorString(e));
   return ok();
 }
 

@@ -7,6 +7,7 @@
 #include <stdint.h>
 #include <string.h>
 #include "wf_chunk_attn.h"
+#include "wf_stream_copy.h"
 
 static int failures = 0;
 #define EXPECT(call, want)                                                          \
@@ -144,6 +145,10 @@ int main(void) {
   if (ca.start != 1560) { printf("evict start %lld\n", (long long)ca.start); ++failures; }
   EXPECT(wf_kv_evict(&ca, 5000, 0, NULL), WF_ERR_RANGE);
   EXPECT(wf_kv_evict(&ca, 1560, WF_EVICT_POISON, NULL), WF_ERR_HIP);
+  EXPECT(wf_stream_copy(QBUF, OBUF, 0, NULL), WF_OK);
+  EXPECT(wf_stream_copy(QBUF, OBUF, 24, NULL), WF_ERR_INVALID_ARG);
+  EXPECT(wf_stream_copy(QBUF, QBUF, 32, NULL), WF_ERR_INVALID_ARG);
+  EXPECT(wf_stream_copy(QBUF, OBUF, 32, NULL), WF_ERR_HIP); /* valid: reaches the (stub) launch */
   EXPECT(wf_kv_append_quantize(&c8, 32760, 1560, QBUF, OBUF, NULL), WF_ERR_CAPACITY);
   EXPECT(wf_kv_append_quantize(&c8, 0, 1560, QBUF, OBUF, NULL), WF_ERR_HIP); /* overwrite in place */
   wf_kv_cache cq = make_cache(WF_FP8_E4M3, 1560, 21, 40, 128);

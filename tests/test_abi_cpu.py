@@ -13,17 +13,18 @@ from chunk_causal_dit_wf_amd import _lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "wf_chunk_attn.h")
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include")) if f.endswith(".h"))
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    text = "".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(wf_[a-z_0-9]+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert {"wf_chunk_attn_fwd", "wf_kv_append", "wf_kv_evict", "wf_last_error"} <= set(names)
+    assert {"wf_chunk_attn_fwd", "wf_kv_append", "wf_kv_evict", "wf_last_error", "wf_stream_copy"} <= set(names)
     L = ctypes.CDLL(_lib.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
@@ -32,8 +33,9 @@ def test_library_exports_every_declared_symbol():
         assert re.search(r"\bT %s$" % n, out, flags=re.M), n
 
 
-def test_header_compiles_as_c():
-    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only", "-x", "c", HEADER],
+@pytest.mark.parametrize("header", HEADERS, ids=os.path.basename)
+def test_header_compiles_as_c(header):
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only", "-x", "c", header],
                        capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
 
@@ -141,6 +143,21 @@ def test_evict_validation():
     assert _status(wf.wf_kv_evict, c, -1) == wf.WF_ERR_RANGE
     wf.wf_kv_evict(c, 40)                     # metadata only, no launch
     assert (c.start, c.end) == (40, 100)
+
+
+def test_stream_copy_validation_before_any_launch():
+    """The reference copy rejects bad sizes, alignment and overlap on the host (nothing is
+    launched: the pointers below are never dereferenced); zero bytes is a no-op."""
+    L = wf.lib()
+    vp = ctypes.c_void_p
+    assert L.wf_stream_copy(vp(4096), vp(1 << 20), 0, None) == wf.WF_OK
+    assert L.wf_stream_copy(vp(4096), vp(1 << 20), 24, None) == wf.WF_ERR_INVALID_ARG      # not 16-byte multiple
+    assert L.wf_stream_copy(vp(4104), vp(1 << 20), 32, None) == wf.WF_ERR_INVALID_ARG      # misaligned source
+    assert L.wf_stream_copy(vp(4096), vp((1 << 20) + 8), 32, None) == wf.WF_ERR_INVALID_ARG
+    assert L.wf_stream_copy(None, vp(1 << 20), 32, None) == wf.WF_ERR_INVALID_ARG
+    assert L.wf_stream_copy(vp(4096), vp(4096 + 64), 128, None) == wf.WF_ERR_INVALID_ARG   # overlap
+    assert L.wf_stream_copy(vp(4096 + 64), vp(4096), 128, None) == wf.WF_ERR_INVALID_ARG
+    assert "overlap" in L.wf_last_error().decode()
 
 
 def test_attention_validation():
