@@ -486,8 +486,8 @@ def extras(args):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py runs on exactly one GPU: multi-GPU runs are not part of this build "
-              "(requested --gpus %d)" % args.gpus, file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path, so there is nothing to "
+              "run on more (requested --gpus %d)" % args.gpus, file=sys.stderr)
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():
