@@ -1,0 +1,120 @@
+"""GPU parity at the documented limits (needs an MI355X).
+
+- A bf16 cache of more than 4 GiB per tensor: the plan takes the
+  register-staged kernel (64-bit page addressing), with the window's pages
+  beyond the 4 GiB line.
+- WF_MAX_CHUNKS = 64 chunks in one call, empty and ragged ones included.
+- A ring of WF_MAX_TABLE_LEN = 256 slots whose live window wraps from the last
+  slot to the first.
+Every case is compared with the float64 oracle at the bf16 bars.
+"""
+import numpy as np
+import pytest
+import torch
+
+import chunk_causal_dit_wf_amd as wf
+from chunk_causal_dit_wf_amd import _lib
+import oracle
+import synth
+from gpu_util import Pair, dev, errors, host_values, values_of
+
+pytestmark = pytest.mark.gpu
+
+BF16_MAX, BF16_MEAN, BF16_REL = 1e-2, 1e-3, 1e-2
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def within_bars(got, ro, what):
+    mx, mean, rel = errors(got, ro)
+    say("%s: max-abs %.3e mean-abs %.3e rel-L2 %.3e" % (what, mx, mean, rel))
+    assert mx <= BF16_MAX and mean <= BF16_MEAN and rel <= BF16_REL, (what, mx, mean, rel)
+
+
+def test_cache_over_4gib_takes_the_staged_kernel():
+    """H1 D128 P64 bf16 with 262208 pages (4.3 GB per tensor); the 16 ring slots map to pages on
+    both sides of the 4 GiB line.  1024 tokens appended, 300 query rows over keys [5, 1000)."""
+    H, D, P = 1, 128, 64
+    per_page = H * P * D * 2
+    num_pages = (1 << 32) // per_page + 64
+    assert num_pages * per_page > (1 << 32)
+    rng = np.random.default_rng([42, 901])
+    table = [num_pages - 1, 262144 + 3, 100, 262150, 7, num_pages - 5, 262144, 33,
+             262200, 1, 262160, 5000, 262170, 262145, 200000, 262190]
+    say("case: cache over 4 GiB, %d pages, table %s" % (num_pages, table))
+    cache = wf.KVCache(num_pages, P, H, D, "bf16", table, device="cuda")
+    n = len(table) * P
+    k = synth.bf16_codes(rng.standard_normal((n, H, D)).astype(np.float32))
+    v = synth.bf16_codes(rng.standard_normal((n, H, D)).astype(np.float32))
+    wf.wf_kv_append(cache, 0, dev(k, "bf16"), dev(v, "bf16"))
+    q = synth.bf16_codes(rng.standard_normal((300, H, D)).astype(np.float32))
+    q_off, kb, ke = [0, 300], [5], [1000]
+    pl = wf.wf_chunk_attn_plan(cache, q_off, kb, ke, "bf16", 0)
+    say("plan:", pl)
+    assert pl["kernel"] == "staged_bf16", pl
+    o, lse = wf.wf_chunk_attn_fwd(cache, dev(q, "bf16"), q_off, kb, ke, return_lse=True, workspace=None)
+    torch.cuda.synchronize()
+    K, V = values_of(k, "bf16"), values_of(v, "bf16")
+    ro, rl = oracle.chunk_attention(values_of(q, "bf16"), K, V, q_off, kb, ke, kv_origin=0)
+    within_bars(host_values(o), ro, "over 4 GiB")
+    assert np.abs(lse.cpu().numpy() - rl).max() < 2e-3
+    del cache, o, lse
+    torch.cuda.empty_cache()
+
+
+def test_max_chunks_in_one_call():
+    """WF_MAX_CHUNKS = 64 chunks (0 to 300 rows, 11 of them empty) over their own windows of a
+    paged bf16 cache (P256, LDS-DMA kernel), in one call."""
+    assert _lib.WF_MAX_CHUNKS == 64
+    say("case: 64 chunks")
+    rng = np.random.default_rng([42, 902])
+    H, D, P, T = 2, 128, 256, 40
+    pair = Pair(T, P, H, D, "bf16", list(rng.permutation(T)), fill_seed=903)
+    n = T * P
+    k = synth.bf16_codes(rng.standard_normal((n, H, D)).astype(np.float32))
+    v = synth.bf16_codes(rng.standard_normal((n, H, D)).astype(np.float32))
+    pair.append(0, k, v)
+    lens = rng.integers(1, 300, size=64)
+    lens[rng.choice(64, size=11, replace=False)] = 0
+    q_off = [0] + np.cumsum(lens).tolist()
+    kb, ke = [], []
+    for _ in range(64):
+        a = int(rng.integers(0, n - 64))
+        b = int(rng.integers(a + 1, min(n, a + 6000) + 1))
+        kb.append(a)
+        ke.append(b)
+    q = synth.bf16_codes(rng.standard_normal((q_off[-1], H, D)).astype(np.float32))
+    pl = wf.wf_chunk_attn_plan(pair.gpu, q_off, kb, ke, "bf16", 0)
+    say("plan:", pl, "rows", q_off[-1])
+    assert pl["kernel"] == "dma_bf16"
+    o, lse = pair.attend(dev(q, "bf16"), q_off, kb, ke, workspace=None)
+    ro, rl = pair.reference(values_of(q, "bf16"), q_off, kb, ke)
+    within_bars(host_values(o), ro, "64 chunks")
+    assert np.abs(lse.cpu().numpy() - rl).max() < 2e-3
+
+
+@pytest.mark.parametrize("P", [64, 40])
+def test_ring_of_max_slots_wraps(P):
+    """WF_MAX_TABLE_LEN = 256 ring slots (P64: LDS-DMA kernel; P40: register-staged): the ring is
+    filled, 8000 tokens are evicted and 8000 more appended, so the live window runs from slot 125
+    (P64) across the last slot to the first; 200 query rows over most of it."""
+    assert _lib.WF_MAX_TABLE_LEN == 256
+    say("case: 256-slot ring, P%d" % P)
+    rng = np.random.default_rng([42, 904, P])
+    H, D, T = 2, 128, 256
+    pair = Pair(T + 8, P, H, D, "bf16", list(rng.permutation(T + 8)[:T]), fill_seed=905)
+    cap = T * P
+    k = synth.bf16_codes(rng.standard_normal((cap + 8000, H, D)).astype(np.float32))
+    v = synth.bf16_codes(rng.standard_normal((cap + 8000, H, D)).astype(np.float32))
+    pair.append(0, k[:cap], v[:cap])
+    pair.evict(8000)
+    pair.append(cap, k[cap:], v[cap:])
+    assert (pair.gpu.start, pair.gpu.end) == (8000, cap + 8000)
+    q = synth.bf16_codes(rng.standard_normal((200, H, D)).astype(np.float32))
+    q_off, kb, ke = [0, 120, 200], [8003, 9000], [cap + 8000, cap + 7001]
+    o, lse = pair.attend(dev(q, "bf16"), q_off, kb, ke, workspace=None)
+    ro, rl = pair.reference(values_of(q, "bf16"), q_off, kb, ke)
+    within_bars(host_values(o), ro, "256-slot ring P%d" % P)
+    assert np.abs(lse.cpu().numpy() - rl).max() < 2e-3
