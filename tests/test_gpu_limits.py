@@ -1,8 +1,8 @@
 """GPU parity at the documented limits (needs an MI355X).
 
-- A bf16 cache of more than 4 GiB per tensor: the plan takes the
+- A bf16 or E4M3FN cache of more than 4 GiB per tensor: the plan takes the
   register-staged kernel (64-bit page addressing), with the window's pages
-  beyond the 4 GiB line.
+  on both sides of the 4 GiB line.
 - WF_MAX_CHUNKS = 64 chunks in one call, empty and ragged ones included.
 - A ring of WF_MAX_TABLE_LEN = 256 slots whose live window wraps from the last
   slot to the first.
@@ -33,32 +33,44 @@ def within_bars(got, ro, what):
     assert mx <= BF16_MAX and mean <= BF16_MEAN and rel <= BF16_REL, (what, mx, mean, rel)
 
 
-def test_cache_over_4gib_takes_the_staged_kernel():
-    """H1 D128 P64 bf16 with 262208 pages (4.3 GB per tensor); the 16 ring slots map to pages on
-    both sides of the 4 GiB line.  1024 tokens appended, 300 query rows over keys [5, 1000)."""
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_cache_over_4gib_takes_the_staged_kernel(dtype):
+    """H1 D128 P64 with more than 4 GiB per tensor (262208 bf16 or 524352 E4M3FN pages); the 16 ring
+    slots map to pages on both sides of the 4 GiB line.  1024 tokens appended, 300 query rows over
+    keys [5, 1000).  The oracle reads the same rows through a 16-page cache model."""
     H, D, P = 1, 128, 64
-    per_page = H * P * D * 2
-    num_pages = (1 << 32) // per_page + 64
+    esize = 2 if dtype == "bf16" else 1
+    per_page = H * P * D * esize
+    line = (1 << 32) // per_page
+    num_pages = line + 64
     assert num_pages * per_page > (1 << 32)
-    rng = np.random.default_rng([42, 901])
-    table = [num_pages - 1, 262144 + 3, 100, 262150, 7, num_pages - 5, 262144, 33,
-             262200, 1, 262160, 5000, 262170, 262145, 200000, 262190]
-    say("case: cache over 4 GiB, %d pages, table %s" % (num_pages, table))
-    cache = wf.KVCache(num_pages, P, H, D, "bf16", table, device="cuda")
+    rng = np.random.default_rng([42, 901, esize])
+    table = [num_pages - 1, line + 3, 100, line + 6, 7, num_pages - 5, line, 33,
+             line + 56, 1, line + 16, 5000, line + 26, line + 1, line // 2, line + 46]
+    say("case: %s cache over 4 GiB, %d pages, table %s" % (dtype, num_pages, table))
+    cache = wf.KVCache(num_pages, P, H, D, dtype, table, device="cuda")
+    ref = oracle.KVCacheModel(len(table), P, H, D, dtype, list(range(len(table))))
     n = len(table) * P
-    k = synth.bf16_codes(rng.standard_normal((n, H, D)).astype(np.float32))
-    v = synth.bf16_codes(rng.standard_normal((n, H, D)).astype(np.float32))
-    wf.wf_kv_append(cache, 0, dev(k, "bf16"), dev(v, "bf16"))
+    kf = rng.standard_normal((n, H, D)).astype(np.float32)
+    vf = rng.standard_normal((n, H, D)).astype(np.float32)
+    if dtype == "bf16":
+        k, v = synth.bf16_codes(kf), synth.bf16_codes(vf)
+        wf.wf_kv_append(cache, 0, dev(k, "bf16"), dev(v, "bf16"))
+        ref.append(0, k, v)
+    else:
+        (k, ks), (v, vs) = synth.quantize_e4m3_pages(kf, P), synth.quantize_e4m3_pages(vf, P)
+        wf.wf_kv_append(cache, 0, dev(k, "fp8"), dev(v, "fp8"), dev(ks, "scale"), dev(vs, "scale"))
+        ref.append(0, k, v, ks, vs)
     q = synth.bf16_codes(rng.standard_normal((300, H, D)).astype(np.float32))
     q_off, kb, ke = [0, 300], [5], [1000]
     pl = wf.wf_chunk_attn_plan(cache, q_off, kb, ke, "bf16", 0)
     say("plan:", pl)
-    assert pl["kernel"] == "staged_bf16", pl
+    assert pl["kernel"] == "staged_" + dtype, pl
     o, lse = wf.wf_chunk_attn_fwd(cache, dev(q, "bf16"), q_off, kb, ke, return_lse=True, workspace=None)
     torch.cuda.synchronize()
-    K, V = values_of(k, "bf16"), values_of(v, "bf16")
+    K, V = ref.gather(0, n)
     ro, rl = oracle.chunk_attention(values_of(q, "bf16"), K, V, q_off, kb, ke, kv_origin=0)
-    within_bars(host_values(o), ro, "over 4 GiB")
+    within_bars(host_values(o), ro, "%s over 4 GiB" % dtype)
     assert np.abs(lse.cpu().numpy() - rl).max() < 2e-3
     del cache, o, lse
     torch.cuda.empty_cache()
