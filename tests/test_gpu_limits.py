@@ -130,3 +130,33 @@ def test_ring_of_max_slots_wraps(P):
     ro, rl = pair.reference(values_of(q, "bf16"), q_off, kb, ke)
     within_bars(host_values(o), ro, "256-slot ring P%d" % P)
     assert np.abs(lse.cpu().numpy() - rl).max() < 2e-3
+
+
+@pytest.mark.parametrize("P", [256, 40])
+@pytest.mark.parametrize("s0", [(1 << 31) - 3000, (1 << 32) - 3000, (1 << 40) + 17])
+def test_long_running_stream_positions(s0, P):
+    """A stream whose logical positions have passed 2^31, 2^32 or 2^40 tokens (about a day of
+    Wan-rate generation passes 2^31): the cache starts at position s0, is filled, 2000 tokens are
+    evicted and 2000 appended, so the window crosses the boundary; cache bytes bit-exact and two
+    chunks' attention against the oracle (P256: LDS-DMA kernel; P40: register-staged)."""
+    say("case: stream positions from %d, P%d" % (s0, P))
+    rng = np.random.default_rng([42, 906, P, s0 % 1000])
+    H, D, T = 2, 128, (24 if P == 256 else 128)  # rings of 6144 and 5120 tokens
+    pair = Pair(T + 4, P, H, D, "bf16", list(rng.permutation(T + 4)[:T]), fill_seed=907)
+    pair.gpu.c.start = pair.gpu.c.end = s0
+    pair.ref.start = pair.ref.end = s0
+    cap = T * P
+    k = synth.bf16_codes(rng.standard_normal((cap + 2000, H, D)).astype(np.float32))
+    v = synth.bf16_codes(rng.standard_normal((cap + 2000, H, D)).astype(np.float32))
+    pair.append(s0, k[:cap], v[:cap])
+    pair.evict(2000)
+    pair.append(s0 + cap, k[cap:], v[cap:])
+    assert (pair.gpu.start, pair.gpu.end) == (s0 + 2000, s0 + cap + 2000)
+    assert pair.pages_equal()
+    q = synth.bf16_codes(rng.standard_normal((300, H, D)).astype(np.float32))
+    q_off = [0, 180, 300]
+    kb, ke = [s0 + 2005, s0 + 3000], [s0 + cap + 2000, s0 + cap + 1000]
+    o, lse = pair.attend(dev(q, "bf16"), q_off, kb, ke, workspace=None)
+    ro, rl = pair.reference(values_of(q, "bf16"), q_off, kb, ke)
+    within_bars(host_values(o), ro, "positions from %d, P%d" % (s0, P))
+    assert np.abs(lse.cpu().numpy() - rl).max() < 2e-3
