@@ -160,3 +160,38 @@ def test_long_running_stream_positions(s0, P):
     ro, rl = pair.reference(values_of(q, "bf16"), q_off, kb, ke)
     within_bars(host_values(o), ro, "positions from %d, P%d" % (s0, P))
     assert np.abs(lse.cpu().numpy() - rl).max() < 2e-3
+
+
+@pytest.mark.parametrize("s0", [(1 << 31) - 3 * 256, (1 << 32) - 12 * 256, 1 << 40])
+def test_long_running_stream_positions_fp8(s0):
+    """The same on an E4M3FN cache (P256, fp8-MFMA kernel): whole-page appends of pre-quantised
+    pages, then 8 pages evicted and 8 appended through the quantising append; cache bytes and
+    scales bit-exact, attention against the oracle at the fp8 bars."""
+    say("case: fp8 stream positions from %d" % s0)
+    P, H, D, T = 256, 2, 128, 24
+    rng = np.random.default_rng([42, 908, s0 % 1000])
+    pair = Pair(T + 4, P, H, D, "fp8", list(rng.permutation(T + 4)[:T]), fill_seed=909)
+    pair.gpu.c.start = pair.gpu.c.end = s0
+    pair.ref.start = pair.ref.end = s0
+    cap = T * P
+    kc, ks = synth.quantize_e4m3_pages(rng.standard_normal((cap, H, D)).astype(np.float32), P)
+    vc, vs = synth.quantize_e4m3_pages(rng.standard_normal((cap, H, D)).astype(np.float32), P)
+    pair.append(s0, kc, vc, ks, vs)
+    pair.evict(8 * P)
+    kn = synth.bf16_codes(rng.standard_normal((8 * P, H, D)).astype(np.float32))
+    vn = synth.bf16_codes(rng.standard_normal((8 * P, H, D)).astype(np.float32))
+    pair.append_quantize(s0 + cap, kn, vn)
+    assert (pair.gpu.start, pair.gpu.end) == (s0 + 8 * P, s0 + cap + 8 * P)
+    assert pair.pages_equal()
+    q = synth.bf16_codes(rng.standard_normal((300, H, D)).astype(np.float32))
+    q_off = [0, 180, 300]
+    kb, ke = [s0 + 8 * P + 5, s0 + 3000], [s0 + cap + 8 * P, s0 + cap + 1000]
+    pl = wf.wf_chunk_attn_plan(pair.gpu, q_off, kb, ke, "bf16", 0)
+    assert pl["kernel"] == "dma_fp8", pl
+    o, lse = pair.attend(dev(q, "bf16"), q_off, kb, ke, workspace=None)
+    ro, rl = pair.reference(values_of(q, "bf16"), q_off, kb, ke)
+    got = host_values(o)
+    mx, mean, rel = errors(got, ro)
+    say("fp8 positions from %d: max-abs %.3e mean-abs %.3e rel-L2 %.3e" % (s0, mx, mean, rel))
+    assert mx <= 5e-2 and rel <= 6e-2, (mx, rel)
+    assert np.abs(lse.cpu().numpy() - rl).max() < 3e-2
