@@ -1120,13 +1120,14 @@ __global__ __launch_bounds__(NTD, 2) void attn_fwd_pp_kernel(const AttnParams p)
 // Merge the partial results of the split schedule: for each row,
 // O = sum_k 2^(m_k - M) O_k / sum_k 2^(m_k - M) l_k with M = max_k m_k (the
 // log-sum-exp combination of attention over disjoint key sets).  One block
-// per (item, kMergeRows rows); the item's partials are its m A parts (slots
-// part * n + item) and, if b > 0, its m B parts.
-template <int D>
+// per (item, kMergeRows rows); the item's NP partials are its m A parts
+// (slots part * n + item) and, if b > 0, its m B parts.  NP is a template
+// argument so that every partial's loads of a row are issued before the first
+// is used.
+template <int D, int NP>
 __global__ __launch_bounds__(256) void attn_merge_kernel(const AttnParams p) {
   constexpr int C4 = D / 4;            // float4 columns per row
   constexpr int RPP = 256 / C4;        // rows per pass
-  constexpr int MAXP = 16;             // partials held in registers
   const SplitSched& sp = p.sp;
   const int nrb = BMD / kMergeRows;
   const int item = blockIdx.x / nrb;
@@ -1134,12 +1135,11 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const AttnParams p) {
   const Item it = decode_item(p, item);
   const ChunkDesc& cd = p.chunk[it.c];
   const int na = sp.n * sp.m;
-  const int np = sp.b > 0 ? 2 * sp.m : sp.m;
-  int slots[MAXP];
+  int slots[NP];
 #pragma unroll
-  for (int k = 0; k < MAXP; ++k) {
+  for (int k = 0; k < NP; ++k) {
     const int part = k % sp.m;
-    slots[k] = k >= np ? 0 : k < sp.m ? part * sp.n + item : na + b_index(p, item, part);
+    slots[k] = k < sp.m ? part * sp.n + item : na + b_index(p, item, part);
   }
   const int tid = threadIdx.x;
   const int c4 = tid % C4;
@@ -1147,23 +1147,25 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const AttnParams p) {
   for (int r = r0 + tid / C4; r < r0 + kMergeRows; r += RPP) {
     const int qrow = it.qt * BMD + r;
     if (qrow >= cd.q_len) break;
-    float mk[MAXP];
+    float mk[NP], lk[NP];
+    f32x4 vk[NP];
+#pragma unroll
+    for (int k = 0; k < NP; ++k) {
+      const float* ws = p.ws + slots[k] * sf;
+      mk[k] = ws[BMD * D + r];
+      lk[k] = ws[BMD * D + BMD + r];
+      vk[k] = *(const f32x4*)(ws + (int64_t)r * D + 4 * c4);
+    }
     float M = -INFINITY;
 #pragma unroll
-    for (int k = 0; k < MAXP; ++k) {
-      mk[k] = k < np ? p.ws[slots[k] * sf + BMD * D + r] : -INFINITY;
-      M = fmaxf(M, mk[k]);
-    }
+    for (int k = 0; k < NP; ++k) M = fmaxf(M, mk[k]);
     float L = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int k = 0; k < MAXP; ++k) {
-      if (k >= np) break;
-      const float* ws = p.ws + slots[k] * sf;
+    for (int k = 0; k < NP; ++k) {
       const float w = __builtin_amdgcn_exp2f(mk[k] - M);
-      L += w * ws[BMD * D + BMD + r];
-      const f32x4 v = *(const f32x4*)(ws + (int64_t)r * D + 4 * c4);
-      acc += w * v;
+      L += w * lk[k];
+      acc += w * vk[k];
     }
     const float inv = 1.f / L;
     const int row = cd.q_begin + qrow;
@@ -1322,13 +1324,22 @@ hipError_t launch_attn_bf16_dma(const AttnParams& p, int head_dim, int grid, hip
   return hipGetLastError();
 }
 
+// The merge instantiation for np partials (1 <= np <= 16: m <= 8 parts, doubled with tails).
+template <int D, int NP = 1>
+static hipError_t launch_merge_np(const AttnParams& p, dim3 grid, hipStream_t s, int np) {
+  if constexpr (NP > 16) {
+    return hipErrorInvalidValue;
+  } else {
+    if (np != NP) return launch_merge_np<D, NP + 1>(p, grid, s, np);
+    hipLaunchKernelGGL((pp::attn_merge_kernel<D, NP>), grid, dim3(256), 0, s, p);
+    return hipGetLastError();
+  }
+}
+
 hipError_t launch_attn_merge(const AttnParams& p, int head_dim, hipStream_t s) {
   const dim3 grid(p.num_items * (kBlockMDma / kMergeRows));
-  if (head_dim == 128)
-    hipLaunchKernelGGL(pp::attn_merge_kernel<128>, grid, dim3(256), 0, s, p);
-  else
-    hipLaunchKernelGGL(pp::attn_merge_kernel<64>, grid, dim3(256), 0, s, p);
-  return hipGetLastError();
+  const int np = p.sp.b > 0 ? 2 * p.sp.m : p.sp.m;
+  return head_dim == 128 ? launch_merge_np<128>(p, grid, s, np) : launch_merge_np<64>(p, grid, s, np);
 }
 
 hipError_t attn_dma_resident_blocks(int head_dim, int* blocks) {
